@@ -1,0 +1,250 @@
+"""Benchmark of the large-chunk TTT layer (update + apply) on one MI355X.
+
+Default workload: 700 frames x 1374 tokens (518x518 frames, patch 14), 8 heads
+of d 128, SwiGLU hidden 256, bf16 tokens and fp32 fast weights, one chunk:
+update on all 961,800 tokens, then apply to all 961,800 queries, renorm on.
+A step is one zm_ttt_update_apply call (weight cast, chunk-gradient partials,
+reduce/step/renorm, apply).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line on stdout.  Besides throughput it reports the roofline
+position of the dominant kernel (algorithmic flops per launch / average launch
+time from HIP events recorded by the library around that kernel on its own
+stream) and the fp64 oracle timed on a bounded sample on this host's cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload f700]
+                  [--cpu-sample-tokens N | --no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector peak
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {"update": "update_bf16.hip", "apply": "apply_bf16.hip"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="f700",
+                   choices=["f700", "f100", "f8", "f700x24", "stream256"])
+    p.add_argument("--seed", type=int, default=4)
+    p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-renorm", action="store_true")
+    return p.parse_args()
+
+
+def source_hash(name):
+    path = os.path.join(ROOT, "reconstruction_lact_chunk_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel, per_launch_units):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_f700.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def make_events(torch, n):
+    evs = []
+    for _ in range(n):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()  # creates the underlying hipEvent_t
+        evs.append(e)
+    return evs
+
+
+def cpu_baseline(inputs_host, sample_tokens, renorm):
+    """The fp64 oracle (as it stands) on the first `sample_tokens` tokens."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    x = {k: v.astype(np.float64) if k in ("w1", "w2", "w3") else v for k, v in inputs_host.items()}
+    t0 = time.perf_counter()
+    oracle.update_apply(x["k"], x["v"], x["eta"], x["q"], x["w1"], x["w2"], x["w3"], renorm=renorm)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the workload, all heads, update+apply "
+                      f"(n_q = n_kv = {sample_tokens}), NumPy fp64, {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the layer's "
+              "multi-GPU sharding is a design note only, not built.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import reconstruction_lact_chunk_amd as zm
+    import workloads as WL
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = WL.WORKLOADS[args.workload]
+    renorm = not args.no_renorm and wl.renorm
+    log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
+        f"h={wl.d_hidden} layers={wl.layers}")
+    x = WL.make_inputs(wl, seed=args.seed, device=dev)
+    layers = [x["w1"], x["w2"], x["w3"]]
+    if wl.layers > 1:
+        ws_layers = [WL.make_weights(wl.heads, wl.d_head, wl.d_hidden, args.seed, dev, layer=i)
+                     for i in range(wl.layers)]
+    else:
+        ws_layers = [tuple(layers)]
+    desc = zm.make_desc(x["w1"], x["w2"], x["w3"], zm.BF16, renorm, x["q"], x["k"])
+    if wl.streaming:
+        p = wl.tokens_per_frame
+        n_ws = zm.workspace_size(desc, p, p)
+    else:
+        n_ws = zm.workspace_size(desc, wl.n_kv, wl.n_q)
+    ws = torch.empty(n_ws, dtype=torch.uint8, device=dev)
+    o = torch.empty_like(x["q"])
+    w_out = [tuple(torch.empty_like(w) for w in wl_w) for wl_w in ws_layers]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(prof=None):
+        if wl.streaming:
+            w = [t.clone() for t in ws_layers[0]]
+            for (s, e) in WL.frame_slices(wl):
+                zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
+                               renorm=renorm, out=o[s:e], workspace=ws)
+            return
+        for li, wl_w in enumerate(ws_layers):
+            if prof is not None:
+                zm.set_profile_events(prof[li])
+            zm.update_apply(x["k"], x["v"], x["eta"], x["q"], *wl_w, renorm=renorm,
+                            w_out=w_out[li], out=o, workspace=ws)
+        if prof is not None:
+            zm.set_profile_events(None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    prof = None
+    if not wl.streaming:
+        prof = [[make_events(torch, 8) for _ in ws_layers] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(K):
+        step(prof[k] if prof else None)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_start.elapsed_time(t_end) / K
+
+    n_tok = wl.n_kv
+    flops_upd = wl.flops_per_token_update() * wl.n_kv
+    flops_app = wl.flops_per_token_apply() * wl.n_q
+    result = {
+        "metric": "TTT update+apply tokens/sec per layer at 700 frames; % bf16 MFMA peak",
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+    }
+    if wl.streaming:
+        frames = wl.frames
+        result["value"] = n_tok / (ms / 1e3)
+        result["per_frame_ms"] = ms / frames
+    else:
+        per_layer_ms = ms / wl.layers
+        result["value"] = n_tok / (per_layer_ms / 1e3)
+        result["layer_frac_bf16_peak"] = round((flops_upd + flops_app) / (per_layer_ms / 1e3) / 1e12
+                                               / PEAK_BF16_TFLOPS, 4)
+        # per-kernel durations from the library's event hooks
+        names = {1: "update", 2: "reduce", 3: "apply", 0: "cast"}
+        durs = {nm: [] for nm in names.values()}
+        for k in range(K):
+            for li in range(len(ws_layers)):
+                ev = prof[k][li]
+                for s, nm in names.items():
+                    durs[nm].append(ev[2 * s].elapsed_time(ev[2 * s + 1]))
+        avg = {nm: float(np.mean(v)) for nm, v in durs.items()}
+        units = {"update": (flops_upd, "update"), "apply": (flops_app, "apply")}
+        kern = {}
+        for nm in ("update", "apply"):
+            fl, _ = units[nm]
+            ach = fl / (avg[nm] / 1e3) / 1e12
+            kern[nm] = {"avg_ms": round(avg[nm], 4), "achieved_tflops": round(ach, 1),
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
+        kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}
+        dom = max(("update", "apply"), key=lambda nm: avg[nm])
+        fl_dom = units[dom][0]
+        ach = fl_dom / (avg[dom] / 1e3) / 1e12
+        result["roofline"] = {
+            "kernel": f"k_update_bf16<128,256>" if dom == "update" else "k_apply_bf16<128,256>",
+            "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(dom, n_tok),
+        }
+        result["kernels"] = kern
+    result["config"] = {
+        "workload": {"f700": "700 frames x 1374 tokens, one chunk: update on 961,800 tokens then "
+                             "apply to 961,800 queries",
+                     "f100": "100 frames x 1374 tokens + one 1374-token target view",
+                     "f8": "8 frames x 1374 tokens",
+                     "f700x24": "700-frame layer x 24 layers with fresh weights per layer",
+                     "stream256": "256 frames x 1374 tokens, one streaming step per frame"}[wl.name],
+        "n_kv": wl.n_kv, "n_q": wl.n_q, "heads": wl.heads, "d_head": wl.d_head,
+        "d_hidden": wl.d_hidden, "layers": wl.layers, "renorm": renorm,
+        "io": "bf16 tokens, fp32 fast weights, fp32 accumulation",
+    }
+    result["wall_s_timed"] = round(wall, 3)
+
+    if not args.no_cpu_baseline:
+        ns = min(args.cpu_sample_tokens, wl.n_kv)
+        host = {k: x[k][:ns].to("cpu", torch.float64).numpy() for k in ("q", "k", "v", "eta")}
+        for k in ("w1", "w2", "w3"):
+            host[k] = x[k].cpu().double().numpy()
+        log(f"cpu baseline: oracle on {ns} tokens")
+        result["cpu_baseline"] = cpu_baseline(host, ns, renorm)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,160 @@
+/*
+ * zm_ttt.h - C ABI of the large-chunk test-time-training (TTT) layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer keeps, per head, a SwiGLU fast weight
+ *     f_W(x) = W2 [ SiLU(W1 x) (*) (W3 x) ]          (elementwise product (*))
+ * with W1, W3 of shape [h, d] and W2 of shape [d, h].  An update takes one
+ * gradient step on the virtual loss  -sum_i eta_i f_W(k_i)^T v_i  summed over
+ * every token of a chunk, optionally renormalises each row of the updated
+ * weights to its pre-update L2 norm, and an apply reads queries through the
+ * weights.
+ *   Sources: "[논문리뷰] ZipMap: Linear-Time Stateful 3D Reconstruction via
+ *   Test-Time Training" (kimjy99.github.io), Method 2. Feature Backbone,
+ *   Eq. (1) (SwiGLU), Eq. (2) (loss), Eq. (3) (chunk gradient with per-token
+ *   rate), the renormalised update display, Eq. (4) (apply), and 3. Streaming
+ *   Reconstruction, Eq. (6); the ZipMap paper-reading notes (67656.sbs),
+ *   sections on Eq. 2 / Eq. 3 and streaming; the mhpn.cn LaCT summary, part
+ *   2、架构 (gradients summed over the whole chunk, L2 normalisation) and
+ *   3、应用场景 (apply/update orders).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Memory: every pointer is device memory owned by the caller.  The library
+ *    allocates nothing, keeps no state between calls (apart from the optional
+ *    profiling events below) and never synchronises the stream.
+ *  - Token tensors q, k, v, o: [n, heads, d_head] with a token stride of
+ *    desc->ld_tok elements (ld_tok >= heads * d_head, multiple of 8).  Element
+ *    type: bf16 or fp32 (desc->io_dtype).  Base pointers 16-byte aligned.
+ *  - eta: fp32 [n, heads], contiguous (token-major), 4-byte aligned.
+ *  - Weights: fp32, contiguous, 16-byte aligned; W1 and W3 [heads, h, d],
+ *    W2 [heads, d, h].  The weights are always fp32; with bf16 io the kernels
+ *    round them to bf16 operands and accumulate in fp32.
+ *  - Workspace: device scratch of at least zm_ttt_workspace_size() bytes,
+ *    256-byte aligned.  Calls sharing one workspace must not overlap in time;
+ *    calls on distinct workspaces and streams are independent.
+ *  - stream: a hipStream_t passed as void*; NULL is the default stream.
+ *    Every entry point only enqueues work and returns.
+ *  - Errors: arguments are checked on the host before any HIP call; a failed
+ *    check returns a negative zm_status and enqueues nothing.  A failed
+ *    launch returns ZM_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronisation.  NaN/Inf inputs propagate (one NaN token
+ *    poisons the chunk sum); they are not checked.
+ *  - Supported shapes: (d_head, d_hidden) in {(64,128), (64,256), (128,128),
+ *    (128,256)}; heads in [1, 64]; others return ZM_ERR_UNSUPPORTED.
+ *  - Results are deterministic: the split of the token sum depends only on
+ *    (n, heads, d_head, d_hidden), and partial sums are combined in a fixed
+ *    order without atomics.
+ */
+#ifndef ZM_TTT_H
+#define ZM_TTT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define ZM_API __attribute__((visibility("default")))
+#else
+#define ZM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum zm_status {
+  ZM_OK = 0,
+  ZM_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or enum */
+  ZM_ERR_UNSUPPORTED = -2,   /* valid but unsupported shape */
+  ZM_ERR_WORKSPACE = -3,     /* workspace missing or too small */
+  ZM_ERR_HIP = -4            /* a HIP launch or runtime call failed */
+} zm_status;
+
+typedef enum zm_dtype { ZM_BF16 = 0, ZM_F32 = 1 } zm_dtype;
+
+/* Row renormalisation after the step: each row r (the fan-in vector of one
+ * output unit: a row of W1 or W3 of length d, a row of W2 of length h) is
+ * rescaled to ||W_r|| / max(||W'_r||, 1e-12) times itself, ||W_r|| being the
+ * norm before the update (review, renormalised update display). */
+typedef enum zm_renorm { ZM_RENORM_NONE = 0, ZM_RENORM_ROW = 1 } zm_renorm;
+
+/* Per-frame order of the streaming step (LaCT summary, 3、应用场景):
+ * APPLY_THEN_UPDATE reads frame t with W(t-1) and then writes it;
+ * UPDATE_THEN_APPLY writes frame t first and reads it with W(t). */
+typedef enum zm_order { ZM_APPLY_THEN_UPDATE = 0, ZM_UPDATE_THEN_APPLY = 1 } zm_order;
+
+typedef struct zm_ttt_desc {
+  int32_t heads;      /* independent fast weights */
+  int32_t d_head;     /* d: width of q, k, v, o per head */
+  int32_t d_hidden;   /* h: SwiGLU hidden width */
+  int32_t io_dtype;   /* zm_dtype of q, k, v, o */
+  int32_t renorm;     /* zm_renorm */
+  int32_t reserved;   /* must be 0 */
+  int64_t ld_tok;     /* elements between consecutive tokens of q/k/v/o */
+} zm_ttt_desc;
+
+/* Bytes of workspace needed by any entry point below for an update over
+ * n_kv tokens and an apply over n_q queries (either may be 0).  Writes the
+ * size to *bytes.  Returns ZM_OK or a validation error. */
+ZM_API int zm_ttt_workspace_size(const zm_ttt_desc* desc, int64_t n_kv, int64_t n_q, size_t* bytes);
+
+/* Update (review Eq. (2)-(3) and the renormalised update display):
+ *   W' = W - grad_W sum_{i<n_kv} eta_i L(f_W(k_i), v_i),  L(f, v) = -f^T v,
+ *   W_hat = renorm(W, W') if desc->renorm else W'.
+ * k, v: [n_kv, heads, d_head] tokens; eta: [n_kv, heads].
+ * w1, w2, w3: the current fast weights (read only).
+ * w1_out, w2_out, w3_out: receive W_hat; they may alias w1, w2, w3 (in-place
+ * update).  n_kv = 0 is valid and gives W_hat = W. */
+ZM_API int zm_ttt_update(const zm_ttt_desc* desc, int64_t n_kv,
+                  const void* k, const void* v, const float* eta,
+                  const float* w1, const float* w2, const float* w3,
+                  float* w1_out, float* w2_out, float* w3_out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Apply (review Eq. (4)): o_i = f_W(q_i) for i < n_q, per head.
+ * q, o: [n_q, heads, d_head] in desc->io_dtype; o must not overlap q. */
+ZM_API int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q,
+                 const float* w1, const float* w2, const float* w3,
+                 void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bidirectional single chunk: the update over all n_kv tokens, then the
+ * apply of all n_q queries through W_hat (the queries may include extra
+ * target-view rows beyond the image tokens).  Outputs W_hat to w*_out (may
+ * alias w*) and o.  Equivalent to zm_ttt_update followed by zm_ttt_apply on
+ * W_hat, without re-reading W_hat from fp32. */
+ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
+                        const void* k, const void* v, const float* eta,
+                        int64_t n_q, const void* q,
+                        const float* w1, const float* w2, const float* w3,
+                        float* w1_out, float* w2_out, float* w3_out, void* o,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* One streaming step on one frame of n_frame tokens (review 3. Streaming
+ * Reconstruction, Eq. (6)).  w1, w2, w3 hold the state W(t-1) on entry and
+ * W(t) on return (updated in place).  q, k, v: [n_frame, heads, d_head];
+ * eta: [n_frame, heads]; o receives f_{W(t-1)}(q) (APPLY_THEN_UPDATE) or
+ * f_{W(t)}(q) (UPDATE_THEN_APPLY). */
+ZM_API int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame,
+                       const void* q, const void* k, const void* v, const float* eta,
+                       float* w1, float* w2, float* w3, void* o,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static description of a status code. */
+ZM_API const char* zm_status_string(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+ZM_API int zm_ttt_version(void);
+
+/* Profiling aid: when events != NULL, every later launch of kernel stage s
+ * (0 weight cast, 1 update partial sums, 2 reduce/step/renorm, 3 apply)
+ * records events[2s] before and events[2s+1] after itself on the launch
+ * stream, for each non-NULL slot.  The events are hipEvent_t handles passed
+ * as void*; n_events must be 8 (or 0 with events == NULL to switch off).
+ * Process-wide setting; not for concurrent use from several threads. */
+ZM_API int zm_ttt_set_profile_events(void* const* events, int n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZM_TTT_H */

@@ -54,14 +54,11 @@ def _blocks(n, block=None):
 # Elementwise functions
 # ---------------------------------------------------------------------------
 def sigmoid(x):
-    """Logistic function 1 / (1 + exp(-x)), split by sign to avoid overflow."""
+    """Logistic function 1 / (1 + exp(-x)), in the form exp(-|x|) / (1 + exp(-|x|))
+    for negative x so that no exponential overflows."""
     x = _f64(x)
-    out = np.empty_like(x)
-    pos = x >= 0
-    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
-    ex = np.exp(x[~pos])
-    out[~pos] = ex / (1.0 + ex)
-    return out
+    z = np.exp(-np.abs(x))
+    return np.where(x >= 0, 1.0 / (1.0 + z), z / (1.0 + z))
 
 
 def silu(x):
@@ -85,8 +82,9 @@ def silu_grad(x):
 def _swiglu_parts(x, w1, w3):
     a = x @ w1.T          # W1 x for every token, [n, h]
     b = x @ w3.T          # W3 x, [n, h]
-    u = silu(a) * b       # SiLU(W1 x) ⊙ (W3 x)
-    return a, b, u
+    sg = sigmoid(a)
+    u = (a * sg) * b      # SiLU(W1 x) ⊙ (W3 x)
+    return a, b, u, sg
 
 
 def swiglu(x, w1, w2, w3, block=None):
@@ -98,7 +96,7 @@ def swiglu(x, w1, w2, w3, block=None):
     x, w1, w2, w3 = map(_f64, (x, w1, w2, w3))
     out = np.empty((x.shape[0], w2.shape[0]))
     for s, e in _blocks(x.shape[0], block):
-        _, _, u = _swiglu_parts(x[s:e], w1, w3)
+        _, _, u, _ = _swiglu_parts(x[s:e], w1, w3)
         out[s:e] = u @ w2.T
     return out
 
@@ -125,11 +123,11 @@ def vjp_swiglu(params, x, cot, block=None):
     g3 = np.zeros_like(w3)
     for s, e in _blocks(x.shape[0], block):
         xb, cb = x[s:e], cot[s:e]
-        a, b, u = _swiglu_parts(xb, w1, w3)
+        a, b, u, sg = _swiglu_parts(xb, w1, w3)
         g2 += cb.T @ u                    # f = W2 u  ->  dW2 = cot u^T
         du = cb @ w2                      # cotangent on u, [n, h]
-        db = du * silu(a)                 # u = SiLU(a) ⊙ b
-        da = du * b * silu_grad(a)
+        db = du * (a * sg)                # u = SiLU(a) ⊙ b
+        da = du * b * (sg * (1.0 + a * (1.0 - sg)))   # SiLU'(a), see silu_grad
         g1 += da.T @ xb                   # a = W1 x  ->  dW1 = da x^T
         g3 += db.T @ xb                   # b = W3 x  ->  dW3 = db x^T
     return g1, g2, g3

@@ -1,0 +1,276 @@
+"""ctypes binding of libzmttt.so (the C ABI declared in include/zm_ttt.h).
+
+Argument marshalling only: every step of the TTT layer runs in the HIP
+library.  torch is used for device memory and for the current HIP stream.
+If the library is missing, every call raises ZmError; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libzmttt.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+BF16, F32 = 0, 1
+RENORM_NONE, RENORM_ROW = 0, 1
+APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+
+EXPORTED = (
+    "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
+    "zm_ttt_stream_step", "zm_status_string", "zm_ttt_version", "zm_ttt_set_profile_events",
+)
+
+
+class ZmError(RuntimeError):
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32),
+        ("d_head", ctypes.c_int32),
+        ("d_hidden", ctypes.c_int32),
+        ("io_dtype", ctypes.c_int32),
+        ("renorm", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("ld_tok", ctypes.c_int64),
+    ]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+_DESC = ctypes.POINTER(Desc)
+
+
+def load_library(path: str | None = None):
+    """Load (once) and return the ctypes handle of libzmttt.so."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ZmError(f"HIP library not found at {p}; build it with "
+                      "`python -m reconstruction_lact_chunk_amd.build_lib`")
+    lib = ctypes.CDLL(p)
+    lib.zm_ttt_workspace_size.argtypes = [_DESC, _I64, _I64, ctypes.POINTER(_SZ)]
+    lib.zm_ttt_update.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.zm_ttt_apply.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.zm_ttt_update_apply.argtypes = [_DESC, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, _SZ, _P]
+    lib.zm_ttt_stream_step.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _P, _SZ, _P]
+    lib.zm_status_string.argtypes = [ctypes.c_int]
+    lib.zm_status_string.restype = ctypes.c_char_p
+    lib.zm_ttt_version.argtypes = []
+    lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
+    for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
+                 "zm_ttt_stream_step", "zm_ttt_version", "zm_ttt_set_profile_events"):
+        getattr(lib, name).restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().zm_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(load_library().zm_ttt_version())
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise ZmError(f"{what}: {status_string(status)} ({status})", status)
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+_IO = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_weights(w1, w2, w3):
+    for w in (w1, w2, w3):
+        if w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 3:
+            raise ZmError("weights must be contiguous fp32 [heads, h, d] / [heads, d, h]")
+        if not w.is_cuda:
+            raise ZmError("weights must be on the GPU")
+    heads, h, d = w1.shape
+    if w3.shape != w1.shape or tuple(w2.shape) != (heads, d, h):
+        raise ZmError("weight shapes disagree: W1, W3 [H, h, d]; W2 [H, d, h]")
+    return heads, d, h
+
+
+def _token_ld(x, heads, d, io):
+    if x is None:
+        return None
+    if x.dtype not in _IO or _IO[x.dtype] != io:
+        raise ZmError("token tensors must all share the io dtype (bf16 or fp32)")
+    if x.dim() != 3 or x.shape[1] != heads or x.shape[2] != d:
+        raise ZmError(f"token tensor shape {tuple(x.shape)} != [n, {heads}, {d}]")
+    if x.shape[0] > 0 and (x.stride(2) != 1 or x.stride(1) != d):
+        raise ZmError("token tensors need unit stride on d and d on heads")
+    if not x.is_cuda:
+        raise ZmError("token tensors must be on the GPU")
+    return x.stride(0) if x.shape[0] > 1 else heads * d
+
+
+def make_desc(w1, w2, w3, io_dtype: int, renorm: bool, *tokens) -> Desc:
+    heads, d, h = _check_weights(w1, w2, w3)
+    lds = {_token_ld(x, heads, d, io_dtype) for x in tokens if x is not None and x.shape[0] > 1}
+    if len(lds) > 1:
+        raise ZmError("all token tensors of one call must share the token stride")
+    ld = lds.pop() if lds else heads * d
+    return Desc(heads, d, h, io_dtype, RENORM_ROW if renorm else RENORM_NONE, 0, ld)
+
+
+def _io_of(*tokens) -> int:
+    for x in tokens:
+        if x is not None:
+            if x.dtype not in _IO:
+                raise ZmError(f"unsupported token dtype {x.dtype}")
+            return _IO[x.dtype]
+    raise ZmError("no token tensor given")
+
+
+def _eta(eta, n, heads):
+    if eta.dtype != torch.float32 or not eta.is_contiguous() or tuple(eta.shape) != (n, heads):
+        raise ZmError(f"eta must be contiguous fp32 [{n}, {heads}]")
+    if not eta.is_cuda:
+        raise ZmError("eta must be on the GPU")
+
+
+def _like_tokens(x):
+    """An output with the same token stride as x (the ABI has one token stride)."""
+    n, heads, d = x.shape
+    if n <= 1 or x.stride(0) == heads * d:
+        return torch.empty((n, heads, d), dtype=x.dtype, device=x.device)
+    buf = torch.empty(n * x.stride(0), dtype=x.dtype, device=x.device)
+    return buf.as_strided((n, heads, d), (x.stride(0), d, 1))
+
+
+def workspace_size(desc: Desc, n_kv: int, n_q: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().zm_ttt_workspace_size(ctypes.byref(desc), int(n_kv), int(n_q),
+                                                 ctypes.byref(out)), "zm_ttt_workspace_size")
+    return int(out.value)
+
+
+def _workspace(desc, n_kv, n_q, device, workspace):
+    need = workspace_size(desc, n_kv, n_q)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ZmError(f"workspace of {workspace.numel()} bytes < {need} needed", ERR_WORKSPACE)
+    return workspace, need
+
+
+def _ws_bytes(ws):
+    return ctypes.c_size_t(ws.numel() * ws.element_size())
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def update(k, v, eta, w1, w2, w3, renorm=False, out=None, workspace=None):
+    """W_hat = step(W; k, v, eta) (+ row renorm).  Returns (W1_hat, W2_hat, W3_hat);
+    pass out=(w1, w2, w3) to update in place."""
+    io = _io_of(k, v)
+    desc = make_desc(w1, w2, w3, io, renorm, k, v)
+    n = k.shape[0]
+    if v.shape[0] != n:
+        raise ZmError("k and v token counts differ")
+    _eta(eta, n, desc.heads)
+    outs = out if out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_weights(*outs)
+    ws, _ = _workspace(desc, n, 0, w1.device, workspace)
+    st = load_library().zm_ttt_update(ctypes.byref(desc), n, _ptr(k), _ptr(v), _ptr(eta),
+                                      _ptr(w1), _ptr(w2), _ptr(w3), *map(_ptr, outs), _ptr(ws),
+                                      _ws_bytes(ws), _stream(w1.device))
+    _check(st, "zm_ttt_update")
+    return outs
+
+
+def apply(q, w1, w2, w3, out=None, workspace=None):
+    """o = f_W(q) per head; q [n, H, d] -> o [n, H, d] (same dtype)."""
+    io = _io_of(q)
+    o = out if out is not None else _like_tokens(q)
+    desc = make_desc(w1, w2, w3, io, False, q, o)
+    n = q.shape[0]
+    ws, _ = _workspace(desc, 0, n, w1.device, workspace)
+    st = load_library().zm_ttt_apply(ctypes.byref(desc), n, _ptr(q), _ptr(w1), _ptr(w2),
+                                     _ptr(w3), _ptr(o), _ptr(ws), _ws_bytes(ws),
+                                     _stream(w1.device))
+    _check(st, "zm_ttt_apply")
+    return o
+
+
+def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, workspace=None):
+    """Bidirectional chunk: update on (k, v, eta), then o = f_{W_hat}(q).
+    Returns ((W1_hat, W2_hat, W3_hat), o)."""
+    io = _io_of(k, v, q)
+    o = out if out is not None else _like_tokens(q)
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o)
+    n_kv, n_q = k.shape[0], q.shape[0]
+    if v.shape[0] != n_kv:
+        raise ZmError("k and v token counts differ")
+    _eta(eta, n_kv, desc.heads)
+    outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_weights(*outs)
+    ws, _ = _workspace(desc, n_kv, n_q, w1.device, workspace)
+    st = load_library().zm_ttt_update_apply(
+        ctypes.byref(desc), n_kv, _ptr(k), _ptr(v), _ptr(eta), n_q, _ptr(q), _ptr(w1), _ptr(w2),
+        _ptr(w3), *map(_ptr, outs), _ptr(o), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
+    _check(st, "zm_ttt_update_apply")
+    return outs, o
+
+
+def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE, out=None,
+                workspace=None):
+    """One frame of the streaming recursion; w1, w2, w3 are updated in place.
+    Returns o (read with W(t-1) for APPLY_THEN_UPDATE, W(t) otherwise)."""
+    io = _io_of(q, k, v)
+    o = out if out is not None else _like_tokens(q)
+    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o)
+    n = q.shape[0]
+    if k.shape[0] != n or v.shape[0] != n:
+        raise ZmError("q, k and v of one frame must have the same token count")
+    _eta(eta, n, desc.heads)
+    ws, _ = _workspace(desc, n, n, w1.device, workspace)
+    st = load_library().zm_ttt_stream_step(ctypes.byref(desc), int(order), n, _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2), _ptr(w3),
+                                           _ptr(o), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
+    _check(st, "zm_ttt_stream_step")
+    return o
+
+
+def set_profile_events(events):
+    """events: 8 torch.cuda.Event (or None entries) recorded around the four
+    kernel stages (cast, update partials, reduce, apply); None switches off."""
+    lib = load_library()
+    if events is None:
+        _check(lib.zm_ttt_set_profile_events(None, 0), "zm_ttt_set_profile_events")
+        return
+    if len(events) != 8:
+        raise ZmError("need 8 event slots")
+    arr = (ctypes.c_void_p * 8)()
+    for i, e in enumerate(events):
+        arr[i] = None if e is None else ctypes.c_void_p(int(e.cuda_event))
+    _check(lib.zm_ttt_set_profile_events(arr, 8), "zm_ttt_set_profile_events")

@@ -1,0 +1,300 @@
+// C-ABI layer of the TTT library: argument validation (host only, before any
+// HIP call), workspace carving and the kernel sequence of each entry point.
+// The entry points, their arguments and error behaviour are specified in
+// include/zm_ttt.h.
+#include "zm_ttt.h"
+
+#include <hip/hip_runtime.h>
+
+#include "zm_internal.h"
+
+using namespace zm;
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+void* g_prof[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+bool g_prof_on = false;
+
+enum Stage { kStageCast = 0, kStageUpdate = 1, kStageReduce = 2, kStageApply = 3 };
+
+inline void prof_mark(int slot, hipStream_t st) {
+  if (g_prof_on && g_prof[slot]) (void)hipEventRecord((hipEvent_t)g_prof[slot], st);
+}
+
+struct Scoped {
+  int stage;
+  hipStream_t st;
+  Scoped(int s, hipStream_t stream) : stage(s), st(stream) { prof_mark(2 * s, st); }
+  ~Scoped() { prof_mark(2 * stage + 1, st); }
+};
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int check_desc(const zm_ttt_desc* d) {
+  if (!d) return ZM_ERR_INVALID_ARG;
+  if (d->heads < 1 || d->d_head < 1 || d->d_hidden < 1) return ZM_ERR_INVALID_ARG;
+  if (d->io_dtype != ZM_BF16 && d->io_dtype != ZM_F32) return ZM_ERR_INVALID_ARG;
+  if (d->renorm != ZM_RENORM_NONE && d->renorm != ZM_RENORM_ROW) return ZM_ERR_INVALID_ARG;
+  if (d->reserved != 0) return ZM_ERR_INVALID_ARG;
+  if (d->ld_tok < (int64_t)d->heads * d->d_head || d->ld_tok % 8 != 0) return ZM_ERR_INVALID_ARG;
+  if (d->heads > 64) return ZM_ERR_UNSUPPORTED;
+  const bool ok_shape = (d->d_head == 64 || d->d_head == 128) &&
+                        (d->d_hidden == 128 || d->d_hidden == 256);
+  if (!ok_shape) return ZM_ERR_UNSUPPORTED;
+  return ZM_OK;
+}
+
+struct Layout {
+  size_t set_a, set_b, part, total;
+  UpdatePlan plan;
+};
+
+// Workspace: two bf16 weight sets (4 arrays each) and the partial sums.
+Layout layout(const zm_ttt_desc* d, int64_t n_kv) {
+  Layout L;
+  const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
+  const size_t set_bytes = round_up(4 * welems * sizeof(uint16_t), 256);
+  L.plan = plan_update(n_kv, d->heads, d->d_hidden);
+  L.set_a = 0;
+  L.set_b = set_bytes;
+  L.part = 2 * set_bytes;
+  L.total = L.part + round_up((size_t)L.plan.splits * 3 * welems * sizeof(float), 256);
+  return L;
+}
+
+WSet carve_set(void* ws, size_t off, size_t welems) {
+  uint16_t* p = (uint16_t*)((char*)ws + off);
+  return WSet{p, p + welems, p + 2 * welems, p + 3 * welems};
+}
+
+int check_counts(int64_t n_kv, int64_t n_q) {
+  const int64_t kMax = (int64_t)1 << 31;  // token indices fit 32-bit tile counts
+  if (n_kv < 0 || n_q < 0 || n_kv > kMax || n_q > kMax) return ZM_ERR_INVALID_ARG;
+  return ZM_OK;
+}
+
+int check_tokens(const void* p, int64_t n) {
+  if (n == 0) return ZM_OK;
+  if (!p || !aligned(p, 16)) return ZM_ERR_INVALID_ARG;
+  return ZM_OK;
+}
+
+int check_eta(const float* p, int64_t n) {
+  if (n == 0) return ZM_OK;
+  if (!p || !aligned(p, 4)) return ZM_ERR_INVALID_ARG;
+  return ZM_OK;
+}
+
+int check_weights(const float* a, const float* b, const float* c) {
+  if (!a || !b || !c) return ZM_ERR_INVALID_ARG;
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(c, 16)) return ZM_ERR_INVALID_ARG;
+  return ZM_OK;
+}
+
+int check_ws(const zm_ttt_desc* d, int64_t n_kv, void* ws, size_t ws_bytes) {
+  const Layout L = layout(d, n_kv);
+  if (!ws) return ZM_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return ZM_ERR_INVALID_ARG;
+  if (ws_bytes < L.total) return ZM_ERR_WORKSPACE;
+  return ZM_OK;
+}
+
+#define ZM_TRY(expr)            \
+  do {                          \
+    const int _s = (expr);      \
+    if (_s != ZM_OK) return _s; \
+  } while (0)
+
+#define ZM_HIP(expr)                          \
+  do {                                        \
+    if ((expr) != hipSuccess) return ZM_ERR_HIP; \
+  } while (0)
+
+// The update part shared by update, update_apply and stream_step: partial
+// sums over n_kv tokens, then the reduce/step/renorm into w*_out.  When
+// emit is non-null the reduce also writes the bf16 copies of W_hat there.
+int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, const float* eta,
+               const float* w1, const float* w2, const float* w3, float* o1, float* o2,
+               float* o3, void* ws, const WSet* emit, bool cast_done, hipStream_t st) {
+  const Layout L = layout(d, n);
+  const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
+  const WSet a = carve_set(ws, L.set_a, welems);
+  float* part = (float*)((char*)ws + L.part);
+  if (n > 0) {
+    if (d->io_dtype == ZM_BF16) {
+      if (!cast_done) {
+        Scoped s(kStageCast, st);
+        ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
+      }
+      Scoped s(kStageUpdate, st);
+      ZM_HIP(launch_update_bf16((const uint16_t*)k, (const uint16_t*)v, eta, n, d->ld_tok,
+                                d->heads, d->d_head, d->d_hidden, a, part, L.plan, st));
+    } else {
+      Scoped s(kStageUpdate, st);
+      ZM_HIP(launch_update_f32((const float*)k, (const float*)v, eta, n, d->ld_tok, d->heads,
+                               d->d_head, d->d_hidden, w1, w2, w3, part, L.plan, st));
+    }
+  }
+  Scoped s(kStageReduce, st);
+  ZM_HIP(launch_reduce(part, L.plan.splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1, o2,
+                       o3, d->renorm, emit, st));
+  return ZM_OK;
+}
+
+// Apply through fp32 weights w* (fp32 path) or through the bf16 set `set`
+// (bf16 path; the caller has filled it).
+int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const float* w1,
+              const float* w2, const float* w3, const WSet& set, hipStream_t st) {
+  if (n == 0) return ZM_OK;
+  Scoped s(kStageApply, st);
+  if (d->io_dtype == ZM_BF16) {
+    ZM_HIP(launch_apply_bf16((const uint16_t*)q, (uint16_t*)o, n, d->ld_tok, d->heads, d->d_head,
+                             d->d_hidden, set, st));
+  } else {
+    ZM_HIP(launch_apply_f32((const float*)q, (float*)o, n, d->ld_tok, d->heads, d->d_head,
+                            d->d_hidden, w1, w2, w3, st));
+  }
+  return ZM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int zm_ttt_version(void) { return kVersion; }
+
+const char* zm_status_string(int status) {
+  switch (status) {
+    case ZM_OK: return "ok";
+    case ZM_ERR_INVALID_ARG: return "invalid argument";
+    case ZM_ERR_UNSUPPORTED: return "unsupported shape";
+    case ZM_ERR_WORKSPACE: return "workspace missing or too small";
+    case ZM_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int zm_ttt_set_profile_events(void* const* events, int n_events) {
+  if (events == nullptr) {
+    if (n_events != 0) return ZM_ERR_INVALID_ARG;
+    for (int i = 0; i < 8; ++i) g_prof[i] = nullptr;
+    g_prof_on = false;
+    return ZM_OK;
+  }
+  if (n_events != 8) return ZM_ERR_INVALID_ARG;
+  for (int i = 0; i < 8; ++i) g_prof[i] = events[i];
+  g_prof_on = true;
+  return ZM_OK;
+}
+
+int zm_ttt_workspace_size(const zm_ttt_desc* desc, int64_t n_kv, int64_t n_q, size_t* bytes) {
+  ZM_TRY(check_desc(desc));
+  ZM_TRY(check_counts(n_kv, n_q));
+  if (!bytes) return ZM_ERR_INVALID_ARG;
+  *bytes = layout(desc, n_kv).total;
+  return ZM_OK;
+}
+
+int zm_ttt_update(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const void* v,
+                  const float* eta, const float* w1, const float* w2, const float* w3,
+                  float* w1_out, float* w2_out, float* w3_out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  ZM_TRY(check_desc(desc));
+  ZM_TRY(check_counts(n_kv, 0));
+  ZM_TRY(check_tokens(k, n_kv));
+  ZM_TRY(check_tokens(v, n_kv));
+  ZM_TRY(check_eta(eta, n_kv));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_weights(w1_out, w2_out, w3_out));
+  ZM_TRY(check_ws(desc, n_kv, workspace, workspace_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  return run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, workspace,
+                    nullptr, false, st);
+}
+
+int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q, const float* w1,
+                 const float* w2, const float* w3, void* o, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  ZM_TRY(check_desc(desc));
+  ZM_TRY(check_counts(0, n_q));
+  ZM_TRY(check_tokens(q, n_q));
+  ZM_TRY(check_tokens(o, n_q));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_ws(desc, 0, workspace, workspace_bytes));
+  if (n_q == 0) return ZM_OK;
+  hipStream_t st = (hipStream_t)stream;
+  const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
+  const Layout L = layout(desc, 0);
+  const WSet a = carve_set(workspace, L.set_a, welems);
+  if (desc->io_dtype == ZM_BF16) {
+    Scoped s(kStageCast, st);
+    ZM_HIP(launch_cast(w1, w2, w3, desc->heads, desc->d_head, desc->d_hidden, a, st));
+  }
+  return run_apply(desc, n_q, q, o, w1, w2, w3, a, st);
+}
+
+int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const void* v,
+                        const float* eta, int64_t n_q, const void* q, const float* w1,
+                        const float* w2, const float* w3, float* w1_out, float* w2_out,
+                        float* w3_out, void* o, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  ZM_TRY(check_desc(desc));
+  ZM_TRY(check_counts(n_kv, n_q));
+  ZM_TRY(check_tokens(k, n_kv));
+  ZM_TRY(check_tokens(v, n_kv));
+  ZM_TRY(check_eta(eta, n_kv));
+  ZM_TRY(check_tokens(q, n_q));
+  ZM_TRY(check_tokens(o, n_q));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_weights(w1_out, w2_out, w3_out));
+  ZM_TRY(check_ws(desc, n_kv, workspace, workspace_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
+  const Layout L = layout(desc, n_kv);
+  const WSet b = carve_set(workspace, L.set_b, welems);
+  const bool bf16 = desc->io_dtype == ZM_BF16;
+  ZM_TRY(run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, workspace,
+                    (bf16 && n_q > 0) ? &b : nullptr, false, st));
+  return run_apply(desc, n_q, q, o, w1_out, w2_out, w3_out, b, st);
+}
+
+int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, const void* q,
+                       const void* k, const void* v, const float* eta, float* w1, float* w2,
+                       float* w3, void* o, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  ZM_TRY(check_desc(desc));
+  if (order != ZM_APPLY_THEN_UPDATE && order != ZM_UPDATE_THEN_APPLY) return ZM_ERR_INVALID_ARG;
+  ZM_TRY(check_counts(n_frame, n_frame));
+  ZM_TRY(check_tokens(q, n_frame));
+  ZM_TRY(check_tokens(k, n_frame));
+  ZM_TRY(check_tokens(v, n_frame));
+  ZM_TRY(check_eta(eta, n_frame));
+  ZM_TRY(check_tokens(o, n_frame));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_ws(desc, n_frame, workspace, workspace_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
+  const Layout L = layout(desc, n_frame);
+  const WSet a = carve_set(workspace, L.set_a, welems);
+  const WSet b = carve_set(workspace, L.set_b, welems);
+  const bool bf16 = desc->io_dtype == ZM_BF16;
+  if (order == ZM_APPLY_THEN_UPDATE) {
+    // Read the frame with W(t-1), then write it; both use one bf16 cast.
+    if (bf16) {
+      Scoped s(kStageCast, st);
+      ZM_HIP(launch_cast(w1, w2, w3, desc->heads, desc->d_head, desc->d_hidden, a, st));
+    }
+    ZM_TRY(run_apply(desc, n_frame, q, o, w1, w2, w3, a, st));
+    return run_update(desc, n_frame, k, v, eta, w1, w2, w3, w1, w2, w3, workspace, nullptr,
+                      true, st);
+  }
+  ZM_TRY(run_update(desc, n_frame, k, v, eta, w1, w2, w3, w1, w2, w3, workspace,
+                    (bf16 && n_frame > 0) ? &b : nullptr, false, st));
+  return run_apply(desc, n_frame, q, o, w1, w2, w3, b, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,239 @@
+// Chunk-gradient kernel of the large-chunk TTT update, bf16 operands on the
+// gfx950 matrix cores (v_mfma_f32_16x16x32_bf16), fp32 accumulation.
+//
+// What it computes (review of ZipMap, kimjy99.github.io, Method 2, Eq. (1)-(3);
+// LaCT summary, mhpn.cn part 二 2、架构): for the SwiGLU fast weight
+// f(x) = W2 [SiLU(W1 x) (*) (W3 x)] and the per-token loss -eta_i f(k_i)^T v_i,
+// minus the gradient summed over a chunk of tokens is
+//     D1 = sum_i  ga_i k_i^T,   D3 = sum_i gb_i k_i^T,   D2 = sum_i eta_i v_i u_i^T
+// with a = W1 k, b = W3 k, s = SiLU(a), u = s (*) b, e = W2^T (eta v) and
+//     ga = e (*) b (*) SiLU'(a),   gb = e (*) s,   SiLU'(a) = sig(a) + s (1 - sig(a)).
+// eta is folded into v once per token (V_eta = eta v), so e, ga, gb carry it
+// and D2 = sum_i u_i (eta_i v_i)^T needs no extra scaling.
+//
+// Work split: a workgroup owns (head, 128 hidden units, one chunk of tokens);
+// each of its 8 waves owns 16 hidden units and keeps, for the whole chunk, its
+// slice of D1^T, D3^T (d x 16) and D2^T (16 x d) in registers, plus its bf16
+// slices of W1, W3, W2^T as MFMA operands.  Per tile of 32 tokens:
+//   forward   A = K W1^T, B = K W3^T, E = V_eta W2   (M = tokens, K = d)
+//   pointwise SiLU / gate backward in registers
+//   backward  D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta  (K = tokens)
+// The forward's token rows are permuted so that each lane's accumulator
+// values are exactly the 8 consecutive tokens the backward B operand needs.
+// The backward reads K and V_eta along tokens, so each tile is staged in LDS
+// twice: token-major (forward) and d-major (backward).
+// The chunk's partial sums go to workspace; a second kernel adds them in a
+// fixed order (no atomics, bitwise reproducible).
+#include "zm_internal.h"
+
+namespace zm {
+
+template <int D, int HID>
+struct UpdCfg {
+  static constexpr int T = kTok;
+  static constexpr int NSL = HID / kHidPerWg;   // hidden slices (workgroups) per head and chunk
+  static constexpr int DP = D + 8;              // token-major row pitch, elements
+  static constexpr int TP = T + 8;              // d-major row pitch, elements
+  static constexpr int KS = D / 32;             // forward k-steps
+  static constexpr int MB = D / 16;             // 16-row blocks along d
+  static constexpr int CPT = D / 8;             // 16-byte chunks per token row
+  static constexpr int ITEMS = T * CPT;         // staging items per tile
+  static constexpr int BUF = 2 * T * DP + 2 * D * TP;  // elements per LDS buffer
+  static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
+};
+
+// SiLU / gate backward for one (token, hidden) element.  a = W1 k, b = W3 k,
+// e = W2^T (eta v).  Returns ga, gb and u = SiLU(a) b.
+__device__ __forceinline__ void gate_backward(float a, float b, float e, float& ga, float& gb,
+                                              float& u) {
+  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
+  const float s = a * sg;
+  u = s * b;
+  gb = e * s;
+  const float dsilu = fmaf(-s, sg, s) + sg;  // sig + s (1 - sig)
+  ga = (e * b) * dsilu;
+}
+
+template <int D, int HID>
+__global__ __launch_bounds__(512) void k_update_bf16(
+    const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
+    const float* __restrict__ eta, int64_t n, int64_t ld, int heads,
+    const uint16_t* __restrict__ w1b, const uint16_t* __restrict__ w3b,
+    const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk) {
+  using C = UpdCfg<D, HID>;
+  constexpr int T = C::T, DP = C::DP, TP = C::TP, KS = C::KS, MB = C::MB, CPT = C::CPT;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::BUF];
+
+  // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
+  // over the 8 XCDs; the slices of one (head, chunk) get ids 8 apart, so they
+  // run on the same XCD at about the same time and share K/V through its L2.
+  const int b = blockIdx.x;
+  const int xcd = b & 7, r = b >> 3;
+  const int slice = r % C::NSL;
+  const int pair = (r / C::NSL) * 8 + xcd;
+  if (pair >= heads * splits) return;
+  const int head = pair % heads, chunk_id = pair / heads;
+  const int64_t t_begin = (int64_t)chunk_id * chunk;
+  const int64_t t_end = (t_begin + chunk < n) ? t_begin + chunk : n;
+  const int ntiles = t_end > t_begin ? (int)ceil_div(t_end - t_begin, T) : 0;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+  const int j0 = slice * kHidPerWg + w * 16;  // first hidden unit of this wave
+
+  // Forward B operands: lane holds W[j0 + c][32 ks + 8 g .. +7].
+  bf16x8 w1f[KS], w3f[KS], w2f[KS];
+  {
+    const int64_t off = ((int64_t)head * HID + j0 + c) * D + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      w1f[ks] = as_bf16x8(*(const u32x4*)(w1b + off + 32 * ks));
+      w3f[ks] = as_bf16x8(*(const u32x4*)(w3b + off + 32 * ks));
+      w2f[ks] = as_bf16x8(*(const u32x4*)(w2tb + off + 32 * ks));
+    }
+  }
+
+  f32x4 acc1[MB], acc3[MB], acc2[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    acc1[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc3[m] = acc1[m];
+    acc2[m] = acc1[m];
+  }
+
+  // ---- staging: one 16-byte chunk of k and of v per thread ---------------
+  const bool has_item = tid < C::ITEMS;
+  const int s_tok = tid / CPT, s_ch = tid - (tid / CPT) * CPT;
+  u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
+  float er = 0.f;
+  auto fetch = [&](int it) {
+    kr = u32x4{0u, 0u, 0u, 0u};
+    vr = kr;
+    er = 0.f;
+    const int64_t t = t_begin + (int64_t)it * T + s_tok;
+    if (has_item && t < t_end) {
+      const int64_t off = t * ld + (int64_t)head * D + 8 * s_ch;
+      kr = *(const u32x4*)(kp + off);
+      vr = *(const u32x4*)(vp + off);
+      er = eta[t * heads + head];
+    }
+  };
+  auto stage = [&](int buf) {
+    if (!has_item) return;
+    uint16_t* base = lds + buf * C::BUF;
+    uint16_t* ktm = base;
+    uint16_t* vtm = base + T * DP;
+    uint16_t* kdm = base + 2 * T * DP;
+    uint16_t* vdm = kdm + D * TP;
+    u32x4 vs;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(vr[q]) * er, bf16hi(vr[q]) * er);
+    *(u32x4*)(ktm + s_tok * DP + 8 * s_ch) = kr;
+    *(u32x4*)(vtm + s_tok * DP + 8 * s_ch) = vs;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int d0 = 8 * s_ch + 2 * q;
+      kdm[d0 * TP + s_tok] = (uint16_t)(kr[q] & 0xffffu);
+      kdm[(d0 + 1) * TP + s_tok] = (uint16_t)(kr[q] >> 16);
+      vdm[d0 * TP + s_tok] = (uint16_t)(vs[q] & 0xffffu);
+      vdm[(d0 + 1) * TP + s_tok] = (uint16_t)(vs[q] >> 16);
+    }
+  };
+
+  auto compute = [&](int buf) {
+    const uint16_t* base = lds + buf * C::BUF;
+    const uint16_t* ktm = base;
+    const uint16_t* vtm = base + T * DP;
+    const uint16_t* kdm = base + 2 * T * DP;
+    const uint16_t* vdm = kdm + D * TP;
+    f32x4 fa[2], fb[2], fe[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      fa[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      fb[mb] = fa[mb];
+      fe[mb] = fa[mb];
+      // MFMA row m of block mb holds token 8 (m / 4) + 4 mb + m % 4, so the
+      // accumulator rows 4g..4g+3 of blocks 0 and 1 are tokens 8g..8g+7.
+      const int row = 8 * (c >> 2) + 4 * mb + (c & 3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ktm + row * DP + 32 * ks + 8 * g));
+        const bf16x8 va = as_bf16x8(*(const u32x4*)(vtm + row * DP + 32 * ks + 8 * g));
+        fa[mb] = mfma_bf16(ka, w1f[ks], fa[mb]);
+        fb[mb] = mfma_bf16(ka, w3f[ks], fb[mb]);
+        fe[mb] = mfma_bf16(va, w2f[ks], fe[mb]);
+      }
+    }
+    // Pointwise backward; element j of each packed operand is token 8g + j.
+    u32x4 gap, gbp, up;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 4; i += 2) {
+        float ga0, gb0, u0, ga1, gb1, u1;
+        gate_backward(fa[mb][i], fb[mb][i], fe[mb][i], ga0, gb0, u0);
+        gate_backward(fa[mb][i + 1], fb[mb][i + 1], fe[mb][i + 1], ga1, gb1, u1);
+        gap[2 * mb + i / 2] = pack_bf16x2(ga0, ga1);
+        gbp[2 * mb + i / 2] = pack_bf16x2(gb0, gb1);
+        up[2 * mb + i / 2] = pack_bf16x2(u0, u1);
+      }
+    }
+    const bf16x8 GA = as_bf16x8(gap), GB = as_bf16x8(gbp), U = as_bf16x8(up);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      // A = K^T rows d = 16 m + c, tokens 8g..8g+7; B = Ga / Gb (tokens x hidden)
+      const bf16x8 kt = as_bf16x8(*(const u32x4*)(kdm + (16 * m + c) * TP + 8 * g));
+      acc1[m] = mfma_bf16(kt, GA, acc1[m]);
+      acc3[m] = mfma_bf16(kt, GB, acc3[m]);
+      // A = U^T (hidden x tokens); B = V_eta, tokens x d = 16 m + c
+      const bf16x8 vt = as_bf16x8(*(const u32x4*)(vdm + (16 * m + c) * TP + 8 * g));
+      acc2[m] = mfma_bf16(U, vt, acc2[m]);
+    }
+  };
+
+  if (ntiles > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const bool more = it + 1 < ntiles;
+    if (more) fetch(it + 1);
+    compute(it & 1);
+    if (more) stage((it + 1) & 1);
+    __syncthreads();
+  }
+
+  // Partial sums in natural weight layouts: [3][h*d] per (chunk, head).
+  const int64_t hd_elems = (int64_t)HID * D;
+  float* P = part + ((int64_t)chunk_id * heads + head) * 3 * hd_elems;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    // acc1/acc3 lane values: D1[j0 + c][16 m + 4 g + i], i = 0..3
+    *(f32x4*)(P + (int64_t)(j0 + c) * D + 16 * m + 4 * g) = acc1[m];
+    *(f32x4*)(P + hd_elems + (int64_t)(j0 + c) * D + 16 * m + 4 * g) = acc3[m];
+    // acc2 lane values: D2^T[j0 + 4 g + i][16 m + c] = D2[16 m + c][j0 + 4 g + i]
+    *(f32x4*)(P + 2 * hd_elems + (int64_t)(16 * m + c) * HID + j0 + 4 * g) = acc2[m];
+  }
+}
+
+hipError_t launch_update_bf16(const uint16_t* k, const uint16_t* v, const float* eta, int64_t n,
+                              int64_t ld, int heads, int d, int h, WSet w, float* part,
+                              UpdatePlan plan, hipStream_t st) {
+  if (plan.splits <= 0) return hipSuccess;
+  const int nsl = h / kHidPerWg;
+  const int64_t pairs = (int64_t)heads * plan.splits;
+  const unsigned blocks = (unsigned)(ceil_div(pairs, 8) * 8 * nsl);
+#define ZM_LAUNCH_UPD(DD, HH)                                                                  \
+  hipLaunchKernelGGL((k_update_bf16<DD, HH>), dim3(blocks), dim3(512), 0, st, k, v, eta, n, ld, \
+                     heads, w.w1b, w.w3b, w.w2tb, part, plan.splits, plan.chunk)
+  if (d == 128 && h == 256) ZM_LAUNCH_UPD(128, 256);
+  else if (d == 128 && h == 128) ZM_LAUNCH_UPD(128, 128);
+  else if (d == 64 && h == 256) ZM_LAUNCH_UPD(64, 256);
+  else if (d == 64 && h == 128) ZM_LAUNCH_UPD(64, 128);
+  else return hipErrorInvalidValue;
+#undef ZM_LAUNCH_UPD
+  return hipGetLastError();
+}
+
+}  // namespace zm

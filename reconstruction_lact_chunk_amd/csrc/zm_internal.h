@@ -1,0 +1,121 @@
+// Internal declarations of the TTT library: vector types, bf16 helpers, the
+// split plan shared by the host planner and the kernels, and the launchers
+// each kernel translation unit exports to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace zm {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;   // MFMA A/B operand (16x16x32)
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;     // MFMA accumulator (16x16)
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;  // 16 raw bytes
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+// ---- tiling constants shared by planner and kernels -----------------------
+constexpr int kTok = 32;          // tokens per LDS tile (bf16 kernels); chunks are multiples
+constexpr int kWaves = 8;         // waves per workgroup of the bf16 kernels
+constexpr int kHidPerWg = 128;    // hidden units owned by one bf16 update workgroup
+constexpr int kHidPerWgF32 = 64;  // hidden units owned by one fp32 update workgroup
+constexpr int kTargetWgs = 256;   // MI355X compute units: one workgroup each
+constexpr int kMinTilesPerChunk = 4;
+
+// bf16 copies of one weight set, [H][h][d] except w2b [H][d][h].
+struct WSet {
+  uint16_t* w1b;   // W1 rows (hidden-major)
+  uint16_t* w3b;   // W3 rows
+  uint16_t* w2b;   // W2 as stored: [d][h]
+  uint16_t* w2tb;  // W2 transposed: [h][d]
+};
+
+__device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round two floats to bf16 (round to nearest even) and pack them, lo first.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);
+  return __builtin_bit_cast(unsigned, b);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---- split plan ------------------------------------------------------------
+struct UpdatePlan {
+  int splits;        // S: token chunks (partial sums) per head
+  int64_t chunk;     // tokens per chunk, a multiple of kTok
+};
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The split is a pure function of (n, heads, d_hidden): results never depend
+// on the device or on occupancy.
+inline UpdatePlan plan_update(int64_t n, int heads, int d_hidden) {
+  UpdatePlan p{0, 0};
+  if (n <= 0) return p;
+  const int nsl = d_hidden / kHidPerWg > 0 ? d_hidden / kHidPerWg : 1;
+  int64_t target = kTargetWgs / (int64_t)(heads * nsl);
+  if (target < 1) target = 1;
+  const int64_t tiles = ceil_div(n, kTok);
+  int64_t s = ceil_div(tiles, kMinTilesPerChunk);
+  if (s > target) s = target;
+  if (s < 1) s = 1;
+  p.chunk = ceil_div(tiles, s) * kTok;
+  p.splits = (int)ceil_div(n, p.chunk);
+  return p;
+}
+
+struct ApplyPlan {
+  int splits;
+  int64_t chunk;
+};
+
+inline ApplyPlan plan_apply(int64_t n, int heads) {
+  ApplyPlan p{0, 0};
+  if (n <= 0) return p;
+  int64_t target = kTargetWgs / heads;
+  if (target < 1) target = 1;
+  const int64_t tiles = ceil_div(n, kTok);
+  int64_t s = tiles < target ? tiles : target;
+  p.chunk = ceil_div(tiles, s) * kTok;
+  p.splits = (int)ceil_div(n, p.chunk);
+  return p;
+}
+
+// ---- launchers (each returns hipSuccess or the launch error) --------------
+hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int heads, int d, int h,
+                       WSet out, hipStream_t st);
+
+hipError_t launch_update_bf16(const uint16_t* k, const uint16_t* v, const float* eta, int64_t n,
+                              int64_t ld, int heads, int d, int h, WSet w, float* part,
+                              UpdatePlan plan, hipStream_t st);
+
+hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
+                         const float* w1, const float* w2, const float* w3,
+                         float* o1, float* o2, float* o3, int renorm, const WSet* out_bf16,
+                         hipStream_t st);
+
+hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
+                             int d, int h, WSet w, hipStream_t st);
+
+hipError_t launch_update_f32(const float* k, const float* v, const float* eta, int64_t n,
+                             int64_t ld, int heads, int d, int h, const float* w1,
+                             const float* w2, const float* w3, float* part, UpdatePlan plan,
+                             hipStream_t st);
+
+hipError_t launch_apply_f32(const float* q, float* o, int64_t n, int64_t ld, int heads, int d,
+                            int h, const float* w1, const float* w2, const float* w3,
+                            hipStream_t st);
+
+}  // namespace zm

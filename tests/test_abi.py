@@ -1,0 +1,176 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/zm_ttt.h declares, and rejects bad arguments on the host with the
+documented status codes before any HIP call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import reconstruction_lact_chunk_amd as zm
+from reconstruction_lact_chunk_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zm_ttt.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(zm.LIB_PATH),
+                                reason="libzmttt.so not built (run the build first)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"ZM_API\s+[\w\s\*]+?\b(zm_\w+)\s*\(", text)))
+
+
+def lib():
+    return zm.load_library()
+
+
+def test_header_declares_what_the_binding_knows():
+    assert declared_functions() == sorted(B.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    L = lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    syms = os.popen(f"nm -D --defined-only {zm.LIB_PATH}").read()
+    exported = set(re.findall(r"\b(zm_\w+)\b", syms))
+    assert exported == set(declared_functions())
+
+
+def test_version_and_status_strings():
+    assert zm.version() == 10000
+    assert zm.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert zm.status_string(s) not in ("ok", "unknown status")
+    assert zm.status_string(-99) == "unknown status"
+
+
+def desc(heads=8, d=128, h=256, io=zm.BF16, renorm=1, ld=None, reserved=0):
+    return zm.Desc(heads, d, h, io, renorm, reserved, heads * d if ld is None else ld)
+
+
+def ws_size(de, n_kv, n_q):
+    out = ctypes.c_size_t(0)
+    st = lib().zm_ttt_workspace_size(ctypes.byref(de), n_kv, n_q, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_structure():
+    de = desc()
+    st0, base = ws_size(de, 0, 0)
+    assert st0 == 0
+    welems = 8 * 256 * 128
+    assert base == 2 * 4 * welems * 2        # two bf16 weight sets, no partial sums
+    st, big = ws_size(de, 961_800, 961_800)
+    assert st == 0
+    parts = (big - base) // (3 * welems * 4)
+    assert (big - base) % (3 * welems * 4) == 0
+    assert 1 <= parts <= 256
+    # more tokens never need fewer partial sums; queries need no workspace
+    sizes = [ws_size(de, n, 0)[1] for n in (1, 31, 32, 33, 1000, 10_992, 137_400, 961_800)]
+    assert sizes == sorted(sizes)
+    assert ws_size(de, 5000, 0)[1] == ws_size(de, 5000, 123_456)[1]
+
+
+@pytest.mark.parametrize("field,value,expect", [
+    ("heads", 0, zm.ERR_INVALID_ARG),
+    ("heads", 65, zm.ERR_UNSUPPORTED),
+    ("d_head", 96, zm.ERR_UNSUPPORTED),
+    ("d_hidden", 512, zm.ERR_UNSUPPORTED),
+    ("d_hidden", 0, zm.ERR_INVALID_ARG),
+    ("io_dtype", 7, zm.ERR_INVALID_ARG),
+    ("renorm", 2, zm.ERR_INVALID_ARG),
+    ("reserved", 1, zm.ERR_INVALID_ARG),
+    ("ld_tok", 8 * 128 - 8, zm.ERR_INVALID_ARG),
+    ("ld_tok", 8 * 128 + 4, zm.ERR_INVALID_ARG),
+])
+def test_bad_descriptor(field, value, expect):
+    de = desc()
+    setattr(de, field, value)
+    if field == "heads" and value > 0:
+        de.ld_tok = value * de.d_head
+    assert ws_size(de, 10, 10)[0] == expect
+
+
+def test_null_descriptor_and_counts():
+    out = ctypes.c_size_t(0)
+    assert lib().zm_ttt_workspace_size(None, 1, 1, ctypes.byref(out)) == zm.ERR_INVALID_ARG
+    de = desc()
+    assert ws_size(de, -1, 0)[0] == zm.ERR_INVALID_ARG
+    assert ws_size(de, 0, -5)[0] == zm.ERR_INVALID_ARG
+    assert lib().zm_ttt_workspace_size(ctypes.byref(de), 1, 1, None) == zm.ERR_INVALID_ARG
+
+
+P = ctypes.c_void_p
+GOOD = P(1 << 20)       # 1 MiB: aligned to anything; never dereferenced here
+ODD = P((1 << 20) + 2)  # misaligned for every check
+
+
+def call_update(de, n, k=GOOD, v=GOOD, eta=GOOD, w=(GOOD, GOOD, GOOD), wo=(GOOD, GOOD, GOOD),
+                ws=GOOD, ws_bytes=0):
+    return lib().zm_ttt_update(ctypes.byref(de), n, k, v, eta, *w, *wo, ws, ws_bytes, None)
+
+
+def test_update_rejects_bad_pointers_before_any_hip_call():
+    de = desc()
+    need = ws_size(de, 100, 0)[1]
+    assert call_update(de, 100, k=None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, v=ODD, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, eta=None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, eta=P((1 << 20) + 1), ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, w=(GOOD, None, GOOD), ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, wo=(GOOD, GOOD, ODD), ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, ws=None, ws_bytes=need) == zm.ERR_WORKSPACE
+    assert call_update(de, 100, ws=P((1 << 20) + 128), ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update(de, 100, ws_bytes=need - 1) == zm.ERR_WORKSPACE
+    assert call_update(de, -3, ws_bytes=need) == zm.ERR_INVALID_ARG
+    bad = desc(d=48)
+    assert call_update(bad, 100, ws_bytes=need) == zm.ERR_UNSUPPORTED
+
+
+def test_apply_update_apply_stream_reject_bad_arguments():
+    L = lib()
+    de = desc()
+    need = ws_size(de, 100, 100)[1]
+    assert L.zm_ttt_apply(ctypes.byref(de), 100, None, GOOD, GOOD, GOOD, GOOD, GOOD, need,
+                          None) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_apply(ctypes.byref(de), 100, GOOD, GOOD, GOOD, GOOD, ODD, GOOD, need,
+                          None) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_apply(ctypes.byref(de), 100, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, 16,
+                          None) == zm.ERR_WORKSPACE
+    assert L.zm_ttt_update_apply(ctypes.byref(de), 100, GOOD, GOOD, GOOD, 100, None, GOOD, GOOD,
+                                 GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need,
+                                 None) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_update_apply(ctypes.byref(de), 100, GOOD, GOOD, GOOD, 100, GOOD, GOOD, GOOD,
+                                 GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need - 256,
+                                 None) == zm.ERR_WORKSPACE
+    for order in (-1, 2):
+        assert L.zm_ttt_stream_step(ctypes.byref(de), order, 100, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                    GOOD, GOOD, GOOD, GOOD, need, None) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_stream_step(ctypes.byref(de), 0, 100, GOOD, GOOD, GOOD, None, GOOD, GOOD,
+                                GOOD, GOOD, GOOD, need, None) == zm.ERR_INVALID_ARG
+
+
+def test_profile_event_argument_checks():
+    L = lib()
+    assert L.zm_ttt_set_profile_events(None, 3) == zm.ERR_INVALID_ARG
+    arr = (ctypes.c_void_p * 8)()
+    assert L.zm_ttt_set_profile_events(arr, 4) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_set_profile_events(arr, 8) == zm.OK
+    assert L.zm_ttt_set_profile_events(None, 0) == zm.OK
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes():
+    w1 = torch.zeros(2, 128, 64)
+    w2 = torch.zeros(2, 64, 128)
+    w3 = torch.zeros(2, 128, 64)
+    q = torch.zeros(10, 2, 64)
+    with pytest.raises(zm.ZmError):
+        zm.apply(q, w1, w2, w3)             # host tensors
+    with pytest.raises(zm.ZmError):
+        zm.make_desc(w1, w2.transpose(1, 2), w3, zm.F32, False)
+    with pytest.raises(zm.ZmError):
+        zm.make_desc(w1.double(), w2, w3, zm.F32, False)

@@ -403,7 +403,16 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
             return vjp(params, O._f64(k), -(e * e)[:, None] * O._f64(v), block=block)
         monkeypatch.setattr(O, "chunk_gradient", cg)
     elif mutation == "silu_grad_as_sigmoid":
-        monkeypatch.setattr(O, "silu_grad", O.sigmoid)
+        orig = O.vjp_swiglu
+
+        def vj(params, x, cot, block=None):
+            # recompute the pull-back with SiLU' replaced by sigmoid
+            w1, w2, w3 = params
+            a, b = x @ w1.T, x @ w3.T
+            sg = O.sigmoid(a)
+            du = cot @ w2
+            return ((du * b * sg).T @ x, cot.T @ (a * sg * b), (du * a * sg).T @ x)
+        monkeypatch.setattr(O, "vjp_swiglu", vj)
     elif mutation == "w2_transposed_in_vjp":
         orig = O.vjp_swiglu
 
@@ -417,7 +426,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mutation):
         def parts(x, w1, w3):
             a = x @ w3.T
             b = x @ w1.T
-            return a, b, O.silu(a) * b
+            sg = O.sigmoid(a)
+            return a, b, a * sg * b, sg
         monkeypatch.setattr(O, "_swiglu_parts", parts)
     elif mutation == "renorm_uses_new_norm":
         def rr(w_old, w_new, eps=O.RENORM_EPS):
