@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=32768)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-renorm", action="store_true")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="first run one plain device copy of this many MiB (a known-size "
+                        "reference dispatch for scaling HBM counters)")
     return p.parse_args()
 
 
@@ -117,6 +120,15 @@ def main():
     renorm = not args.no_renorm and wl.renorm
     log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
         f"h={wl.d_hidden} layers={wl.layers}")
+    if args.copy_calibration_mib > 0:
+        nb = args.copy_calibration_mib << 20
+        src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {nb} bytes read, {nb} bytes written")
+        del src, dst
     x = WL.make_inputs(wl, seed=args.seed, device=dev)
     layers = [x["w1"], x["w2"], x["w3"]]
     if wl.layers > 1:

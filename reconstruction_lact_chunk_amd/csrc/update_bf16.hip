@@ -18,10 +18,15 @@
 //   forward   A = K W1^T, B = K W3^T, E = V_eta W2   (M = tokens, K = d)
 //   pointwise SiLU / gate backward in registers
 //   backward  D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta  (K = tokens)
-// The forward's token rows are permuted so that each lane's accumulator
-// values are exactly the 8 consecutive tokens the backward B operand needs.
-// The backward reads K and V_eta along tokens, so each tile is staged in LDS
-// twice: token-major (forward) and d-major (backward).
+// The backward contracts over tokens, so its K / V_eta operands are read
+// from the token-major LDS tile with the gfx950 transposing LDS load
+// (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte words loaded by lanes 4e + i / 4 (e = 0..3), which turns
+// four 4-column row pieces into four 4-row column pieces.  The forward's
+// token rows are permuted (token map tau below) so that each lane's forward
+// accumulators are exactly the tokens its backward operand slots hold, and
+// the tile rows are XOR-swizzled in 16-byte chunks so that both the forward
+// row reads and the transposing reads are free of LDS bank conflicts.
 // The chunk's partial sums go to workspace; a second kernel adds them in a
 // fixed order (no atomics, bitwise reproducible).
 #include "zm_internal.h"
@@ -32,15 +37,39 @@ template <int D, int HID>
 struct UpdCfg {
   static constexpr int T = kTok;
   static constexpr int NSL = HID / kHidPerWg;   // hidden slices (workgroups) per head and chunk
-  static constexpr int DP = D + 8;              // token-major row pitch, elements
-  static constexpr int TP = T + 8;              // d-major row pitch, elements
   static constexpr int KS = D / 32;             // forward k-steps
   static constexpr int MB = D / 16;             // 16-row blocks along d
   static constexpr int CPT = D / 8;             // 16-byte chunks per token row
   static constexpr int ITEMS = T * CPT;         // staging items per tile
-  static constexpr int BUF = 2 * T * DP + 2 * D * TP;  // elements per LDS buffer
+  static constexpr int BUF = 2 * T * D;         // elements per LDS buffer (K tile, V_eta tile)
   static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
 };
+
+// Tile layout: row r (token) of D bf16, 16-byte chunk ch stored at chunk
+// ch ^ swz(r).  With the token map tau, the 16 rows one forward read touches
+// and the 8 rows one half-wave transposing read touches fall in distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  constexpr int half = D / 16;                  // chunks per row / 2
+  constexpr int sh = D == 128 ? 0 : 1;
+  return 2 * ((r >> sh) & (half - 1)) + ((r >> 4) & 1);
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int col) {  // col multiple of 4
+  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+}
+// Token held in operand slot j (0..7) by the lanes of 16-lane group g.
+__device__ __forceinline__ int tau(int g, int j) {
+  return 16 * (g >> 1) + 4 * (g & 1) + 8 * (j >> 2) + (j & 3);
+}
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (lds_bf16x4*)((__attribute__((address_space(3))) void*)(p)));
+}
 
 // SiLU / gate backward for one (token, hidden) element.  a = W1 k, b = W3 k,
 // e = W2^T (eta v).  Returns ga, gb and u = SiLU(a) b.
@@ -61,7 +90,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const uint16_t* __restrict__ w1b, const uint16_t* __restrict__ w3b,
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk) {
   using C = UpdCfg<D, HID>;
-  constexpr int T = C::T, DP = C::DP, TP = C::TP, KS = C::KS, MB = C::MB, CPT = C::CPT;
+  constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT;
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::BUF];
 
   // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
@@ -120,51 +149,43 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   };
   auto stage = [&](int buf) {
     if (!has_item) return;
-    uint16_t* base = lds + buf * C::BUF;
-    uint16_t* ktm = base;
-    uint16_t* vtm = base + T * DP;
-    uint16_t* kdm = base + 2 * T * DP;
-    uint16_t* vdm = kdm + D * TP;
+    uint16_t* ktm = lds + buf * C::BUF;
+    uint16_t* vtm = ktm + T * D;
     u32x4 vs;
 #pragma unroll
     for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(vr[q]) * er, bf16hi(vr[q]) * er);
-    *(u32x4*)(ktm + s_tok * DP + 8 * s_ch) = kr;
-    *(u32x4*)(vtm + s_tok * DP + 8 * s_ch) = vs;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int d0 = 8 * s_ch + 2 * q;
-      kdm[d0 * TP + s_tok] = (uint16_t)(kr[q] & 0xffffu);
-      kdm[(d0 + 1) * TP + s_tok] = (uint16_t)(kr[q] >> 16);
-      vdm[d0 * TP + s_tok] = (uint16_t)(vs[q] & 0xffffu);
-      vdm[(d0 + 1) * TP + s_tok] = (uint16_t)(vs[q] >> 16);
-    }
+    const int off = tile_off<D>(s_tok, 8 * s_ch);
+    *(u32x4*)(ktm + off) = kr;
+    *(u32x4*)(vtm + off) = vs;
   };
 
+  // Transposing-read addresses: lane (g, s) loads 4 columns 16 m + 4 (s % 4)
+  // of rows tau(g, s / 4) (slots 0..3) and tau(g, 4 + s / 4) (slots 4..7).
+  const int row_a = tau(g, c >> 2), row_b = row_a + 8;  // swz(row_b) == swz(row_a)
+
   auto compute = [&](int buf) {
-    const uint16_t* base = lds + buf * C::BUF;
-    const uint16_t* ktm = base;
-    const uint16_t* vtm = base + T * DP;
-    const uint16_t* kdm = base + 2 * T * DP;
-    const uint16_t* vdm = kdm + D * TP;
+    const uint16_t* ktm = lds + buf * C::BUF;
+    const uint16_t* vtm = ktm + T * D;
     f32x4 fa[2], fb[2], fe[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       fa[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
       fb[mb] = fa[mb];
       fe[mb] = fa[mb];
-      // MFMA row m of block mb holds token 8 (m / 4) + 4 mb + m % 4, so the
-      // accumulator rows 4g..4g+3 of blocks 0 and 1 are tokens 8g..8g+7.
-      const int row = 8 * (c >> 2) + 4 * mb + (c & 3);
+      // MFMA row m = 4 g' + i of block mb holds token tau(g', 4 mb + i), so a
+      // lane's accumulator rows are the tokens of its backward slots.
+      const int row = tau(c >> 2, 4 * mb + (c & 3));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ktm + row * DP + 32 * ks + 8 * g));
-        const bf16x8 va = as_bf16x8(*(const u32x4*)(vtm + row * DP + 32 * ks + 8 * g));
+        const int off = tile_off<D>(row, 32 * ks + 8 * g);
+        const bf16x8 ka = as_bf16x8(*(const u32x4*)(ktm + off));
+        const bf16x8 va = as_bf16x8(*(const u32x4*)(vtm + off));
         fa[mb] = mfma_bf16(ka, w1f[ks], fa[mb]);
         fb[mb] = mfma_bf16(ka, w3f[ks], fb[mb]);
         fe[mb] = mfma_bf16(va, w2f[ks], fe[mb]);
       }
     }
-    // Pointwise backward; element j of each packed operand is token 8g + j.
+    // Pointwise backward; slot j of each packed operand is token tau(g, j).
     u32x4 gap, gbp, up;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -181,12 +202,16 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const bf16x8 GA = as_bf16x8(gap), GB = as_bf16x8(gbp), U = as_bf16x8(up);
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-      // A = K^T rows d = 16 m + c, tokens 8g..8g+7; B = Ga / Gb (tokens x hidden)
-      const bf16x8 kt = as_bf16x8(*(const u32x4*)(kdm + (16 * m + c) * TP + 8 * g));
+      const int col = 16 * m + 4 * (c & 3);
+      const int oa = tile_off<D>(row_a, col), ob = tile_off<D>(row_b, col);
+      // A = K^T: rows d = 16 m + c, slots = tokens tau(g, 0..7); B = Ga / Gb
+      const bf16x8 kt = __builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
       acc1[m] = mfma_bf16(kt, GA, acc1[m]);
       acc3[m] = mfma_bf16(kt, GB, acc3[m]);
-      // A = U^T (hidden x tokens); B = V_eta, tokens x d = 16 m + c
-      const bf16x8 vt = as_bf16x8(*(const u32x4*)(vdm + (16 * m + c) * TP + 8 * g));
+      // A = U^T (hidden x tokens); B = V_eta (tokens x d = 16 m + c)
+      const bf16x8 vt = __builtin_shufflevector(lds_read_tr(vtm + oa), lds_read_tr(vtm + ob),
+                                                0, 1, 2, 3, 4, 5, 6, 7);
       acc2[m] = mfma_bf16(U, vt, acc2[m]);
     }
   };
