@@ -37,9 +37,10 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *COMMON, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, defines=(), build_dir=BUILD) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    defs = [f"-D{d}" for d in defines]
+    cmd = [hipcc(), *COMMON, *defs, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -50,21 +51,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libzmttt.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link the library (default: libzmttt.so next
+    to this file); `defines` are extra preprocessor definitions such as tuning
+    switches.  Returns the library path."""
+    build_dir = BUILD if out == LIB else out + ".objs"
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), SOURCES))
+    tmp = out + ".tmp"
     cmd = [hipcc(), *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="--verbose" in sys.argv))
+    defs = [a[2:] for a in sys.argv[1:] if a.startswith("-D")]
+    outs = [a.split("=", 1)[1] for a in sys.argv[1:] if a.startswith("--out=")]
+    print(build(verbose="--verbose" in sys.argv, defines=defs, out=outs[0] if outs else LIB))

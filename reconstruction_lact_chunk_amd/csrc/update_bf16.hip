@@ -18,6 +18,7 @@
 //   forward   A = K W1^T, B = K W3^T, E = V_eta W2   (M = tokens, K = d)
 //   pointwise SiLU / gate backward in registers
 //   backward  D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta  (K = tokens)
+// software-pipelined over tiles (see the main loop).
 // The backward contracts over tokens, so its K / V_eta operands are read
 // from the token-major LDS tile with the gfx950 transposing LDS load
 // (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
@@ -30,6 +31,20 @@
 // The chunk's partial sums go to workspace; a second kernel adds them in a
 // fixed order (no atomics, bitwise reproducible).
 #include "zm_internal.h"
+
+// Schedule knobs of the steady-state loop (compile-time; defaults are the
+// measured best): LDS fetch lookahead in slots, slot order (0: all backward
+// slots then all forward slots; 1: alternating), and whether MFMA issue
+// runs at raised wave priority.
+#ifndef ZM_LOOKAHEAD
+#define ZM_LOOKAHEAD 1
+#endif
+#ifndef ZM_ORDER
+#define ZM_ORDER 0
+#endif
+#ifndef ZM_PRIO
+#define ZM_PRIO 0
+#endif
 
 namespace zm {
 
@@ -91,7 +106,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk) {
   using C = UpdCfg<D, HID>;
   constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * C::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * C::BUF];
 
   // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
   // over the 8 XCDs; the slices of one (head, chunk) get ids 8 apart, so they
@@ -135,21 +150,34 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   const int s_tok = tid / CPT, s_ch = tid - (tid / CPT) * CPT;
   u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
   float er = 0.f;
+  // Per-lane element offsets of this thread's staging chunk inside a tile;
+  // the tile base is uniform, so loads use a scalar base + vector offset.
+  const int lane_tok_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
+  const int lane_eta_off = (has_item ? s_tok : 0) * heads + head;
   auto fetch = [&](int it) {
-    kr = u32x4{0u, 0u, 0u, 0u};
-    vr = kr;
-    er = 0.f;
-    const int64_t t = t_begin + (int64_t)it * T + s_tok;
-    if (has_item && t < t_end) {
-      const int64_t off = t * ld + (int64_t)head * D + 8 * s_ch;
-      kr = *(const u32x4*)(kp + off);
-      vr = *(const u32x4*)(vp + off);
-      er = eta[t * heads + head];
+    const int64_t t0 = t_begin + (int64_t)it * T;
+    if (t0 + T <= t_end) {  // whole tile in range (uniform branch)
+      kr = *(const u32x4*)(kp + t0 * ld + lane_tok_off);
+      vr = *(const u32x4*)(vp + t0 * ld + lane_tok_off);
+      er = eta[t0 * heads + lane_eta_off];
+    } else {
+      // Tail tile: out-of-range tokens get eta = 0 and the tile's first
+      // token's k and v (finite values; eta = 0 zeroes their contribution,
+      // since e, ga, gb and V_eta all carry eta).
+      const bool ok = has_item && t0 + s_tok < t_end;
+      const int64_t tc = ok ? t0 + s_tok : t0;
+      const int col = has_item ? 8 * s_ch : 0;
+      kr = *(const u32x4*)(kp + tc * ld + head * D + col);
+      vr = *(const u32x4*)(vp + tc * ld + head * D + col);
+      const float e0 = eta[tc * heads + head];
+      er = ok ? e0 : 0.f;
     }
   };
   auto stage = [&](int buf) {
-    if (!has_item) return;
-    uint16_t* ktm = lds + buf * C::BUF;
+    if constexpr (C::ITEMS < kWaves * 64) {
+      if (!has_item) return;
+    }
+    uint16_t* ktm = lds + (buf & 3) * C::BUF;
     uint16_t* vtm = ktm + T * D;
     u32x4 vs;
 #pragma unroll
@@ -163,15 +191,23 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   // of rows tau(g, s / 4) (slots 0..3) and tau(g, 4 + s / 4) (slots 4..7).
   const int row_a = tau(g, c >> 2), row_b = row_a + 8;  // swz(row_b) == swz(row_a)
 
-  auto compute = [&](int buf) {
-    const uint16_t* ktm = lds + buf * C::BUF;
+  struct Fwd {
+    f32x4 a[2], b[2], e[2];
+  };
+  struct Grad {
+    bf16x8 ga, gb, u;
+  };
+
+  // forward A = K W1^T, B = K W3^T, E = V_eta W2 on one tile (24 MFMAs)
+  auto forward = [&](int buf) {
+    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
     const uint16_t* vtm = ktm + T * D;
-    f32x4 fa[2], fb[2], fe[2];
+    Fwd f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      fa[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      fb[mb] = fa[mb];
-      fe[mb] = fa[mb];
+      f.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      f.b[mb] = f.a[mb];
+      f.e[mb] = f.a[mb];
       // MFMA row m = 4 g' + i of block mb holds token tau(g', 4 mb + i), so a
       // lane's accumulator rows are the tokens of its backward slots.
       const int row = tau(c >> 2, 4 * mb + (c & 3));
@@ -180,26 +216,36 @@ __global__ __launch_bounds__(512) void k_update_bf16(
         const int off = tile_off<D>(row, 32 * ks + 8 * g);
         const bf16x8 ka = as_bf16x8(*(const u32x4*)(ktm + off));
         const bf16x8 va = as_bf16x8(*(const u32x4*)(vtm + off));
-        fa[mb] = mfma_bf16(ka, w1f[ks], fa[mb]);
-        fb[mb] = mfma_bf16(ka, w3f[ks], fb[mb]);
-        fe[mb] = mfma_bf16(va, w2f[ks], fe[mb]);
+        f.a[mb] = mfma_bf16(ka, w1f[ks], f.a[mb]);
+        f.b[mb] = mfma_bf16(ka, w3f[ks], f.b[mb]);
+        f.e[mb] = mfma_bf16(va, w2f[ks], f.e[mb]);
       }
     }
-    // Pointwise backward; slot j of each packed operand is token tau(g, j).
+    return f;
+  };
+
+  // pointwise SiLU / gate backward (VALU); slot j of each operand is token tau(g, j)
+  auto pointwise = [&](const Fwd& f) {
     u32x4 gap, gbp, up;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         float ga0, gb0, u0, ga1, gb1, u1;
-        gate_backward(fa[mb][i], fb[mb][i], fe[mb][i], ga0, gb0, u0);
-        gate_backward(fa[mb][i + 1], fb[mb][i + 1], fe[mb][i + 1], ga1, gb1, u1);
+        gate_backward(f.a[mb][i], f.b[mb][i], f.e[mb][i], ga0, gb0, u0);
+        gate_backward(f.a[mb][i + 1], f.b[mb][i + 1], f.e[mb][i + 1], ga1, gb1, u1);
         gap[2 * mb + i / 2] = pack_bf16x2(ga0, ga1);
         gbp[2 * mb + i / 2] = pack_bf16x2(gb0, gb1);
         up[2 * mb + i / 2] = pack_bf16x2(u0, u1);
       }
     }
-    const bf16x8 GA = as_bf16x8(gap), GB = as_bf16x8(gbp), U = as_bf16x8(up);
+    return Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
+  };
+
+  // backward D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta (24 MFMAs)
+  auto backward = [&](int buf, const Grad& gr) {
+    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const uint16_t* vtm = ktm + T * D;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int col = 16 * m + 4 * (c & 3);
@@ -207,26 +253,140 @@ __global__ __launch_bounds__(512) void k_update_bf16(
       // A = K^T: rows d = 16 m + c, slots = tokens tau(g, 0..7); B = Ga / Gb
       const bf16x8 kt = __builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
                                                 0, 1, 2, 3, 4, 5, 6, 7);
-      acc1[m] = mfma_bf16(kt, GA, acc1[m]);
-      acc3[m] = mfma_bf16(kt, GB, acc3[m]);
+      acc1[m] = mfma_bf16(kt, gr.ga, acc1[m]);
+      acc3[m] = mfma_bf16(kt, gr.gb, acc3[m]);
       // A = U^T (hidden x tokens); B = V_eta (tokens x d = 16 m + c)
       const bf16x8 vt = __builtin_shufflevector(lds_read_tr(vtm + oa), lds_read_tr(vtm + ob),
                                                 0, 1, 2, 3, 4, 5, 6, 7);
-      acc2[m] = mfma_bf16(U, vt, acc2[m]);
+      acc2[m] = mfma_bf16(gr.u, vt, acc2[m]);
     }
   };
 
+  // ---- one "slot" = one operand fetch from LDS + 3 MFMAs ------------------
+  struct Frag2 {
+    bf16x8 x, y;
+  };
+  auto fwd_frag = [&](int buf, int mb, int ks) {  // K and V_eta rows (A operands)
+    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const int off = tile_off<D>(tau(c >> 2, 4 * mb + (c & 3)), 32 * ks + 8 * g);
+    return Frag2{as_bf16x8(*(const u32x4*)(ktm + off)),
+                 as_bf16x8(*(const u32x4*)(ktm + T * D + off))};
+  };
+  auto fwd_mma = [&](Fwd& f, int mb, int ks, const Frag2& fr) {
+    f.a[mb] = mfma_bf16(fr.x, w1f[ks], f.a[mb]);
+    f.b[mb] = mfma_bf16(fr.x, w3f[ks], f.b[mb]);
+    f.e[mb] = mfma_bf16(fr.y, w2f[ks], f.e[mb]);
+  };
+  auto bwd_frag = [&](int buf, int m) {  // K^T and V_eta^T column pieces
+    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const int col = 16 * m + 4 * (c & 3);
+    const int oa = tile_off<D>(row_a, col), ob = tile_off<D>(row_b, col);
+    return Frag2{__builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
+                                         0, 1, 2, 3, 4, 5, 6, 7),
+                 __builtin_shufflevector(lds_read_tr(ktm + T * D + oa),
+                                         lds_read_tr(ktm + T * D + ob), 0, 1, 2, 3, 4, 5, 6, 7)};
+  };
+  auto bwd_mma = [&](int m, const Frag2& fr, const Grad& gr) {
+    acc1[m] = mfma_bf16(fr.x, gr.ga, acc1[m]);
+    acc3[m] = mfma_bf16(fr.x, gr.gb, acc3[m]);
+    acc2[m] = mfma_bf16(gr.u, fr.y, acc2[m]);
+  };
+
+  // Software pipeline over tiles, four LDS buffers (tile t in buffer t % 4).
+  // Iteration t (steady state) is 16 slots: backward(t - 1) in slots 0..7 and
+  // forward(t + 1) in slots 8..15, each slot's LDS fetch issued two slots
+  // ahead; the pointwise backward of tile t is spread over the slots (half of
+  // one element row per slot) so its VALU and transcendental work runs while
+  // the MFMAs of the same wave are in flight.  Staging of tile t + 2 and one
+  // barrier close the iteration.  The fences keep this order through the
+  // compiler's scheduler.
   if (ntiles > 0) {
     fetch(0);
     stage(0);
-  }
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
-    if (more) fetch(it + 1);
-    compute(it & 1);
-    if (more) stage((it + 1) & 1);
+    fetch(1);
+    stage(1);
     __syncthreads();
+    Fwd f = forward(0);
+    Grad prev;
+    {  // t = 0: no backward yet
+      fetch(2);
+      const Grad cur = pointwise(f);
+      if (ntiles > 1) f = forward(1);
+      stage(2);
+      __syncthreads();
+      prev = cur;
+    }
+    constexpr int NB = MB;            // backward slots
+    constexpr int NF = 2 * KS;        // forward slots
+    constexpr int NSLOT = NB + NF;
+    for (int t = 1; t + 1 < ntiles; ++t) {  // steady state
+      fetch(t + 2);
+      Fwd fn;
+      float p_s[8], p_sg[8], p_ga[8], p_gb[8], p_u[8];
+      u32x4 gap, gbp, up;
+      // Slot j runs backward block bslot(j) or forward step fslot(j).
+      auto is_bwd = [&](int j) { return ZM_ORDER == 0 ? j < NB : (j & 1) == 0; };
+      auto bidx = [&](int j) { return ZM_ORDER == 0 ? j : j >> 1; };
+      auto fidx = [&](int j) { return ZM_ORDER == 0 ? j - NB : j >> 1; };
+      auto load_slot = [&](int j) {
+        return is_bwd(j) ? bwd_frag(t - 1, bidx(j)) : fwd_frag(t + 1, fidx(j) / KS, fidx(j) % KS);
+      };
+      Frag2 fr[NSLOT];
+#pragma unroll
+      for (int j = 0; j < ZM_LOOKAHEAD; ++j) fr[j] = load_slot(j);
+#pragma unroll
+      for (int j = 0; j < NSLOT; ++j) {
+        if (j + ZM_LOOKAHEAD < NSLOT) fr[j + ZM_LOOKAHEAD] = load_slot(j + ZM_LOOKAHEAD);
+        if (ZM_PRIO) __builtin_amdgcn_s_setprio(1);
+        if (is_bwd(j)) {
+          bwd_mma(bidx(j), fr[j], prev);
+        } else {
+          const int mb = fidx(j) / KS, ks = fidx(j) % KS;
+          if (ks == 0) {  // first k-step: start from zero accumulators
+            fn.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            fn.b[mb] = fn.a[mb];
+            fn.e[mb] = fn.a[mb];
+          }
+          fwd_mma(fn, mb, ks, fr[j]);
+        }
+        if (ZM_PRIO) __builtin_amdgcn_s_setprio(0);
+        // Each slot does the pointwise halves h in [16 j / NSLOT, 16 (j + 1) / NSLOT):
+        // even h: sigmoid and SiLU of element row h / 2; odd h: its gradients.
+#pragma unroll
+        for (int h = (16 * j) / NSLOT; h < (16 * (j + 1)) / NSLOT; ++h) {
+          const int r = h >> 1, mb = r >> 2, i = r & 3;
+          if ((h & 1) == 0) {
+            const float a = f.a[mb][i];
+            const float sg = __builtin_amdgcn_rcpf(
+                1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
+            p_sg[r] = sg;
+            p_s[r] = a * sg;
+          } else {
+            const float b = f.b[mb][i], e = f.e[mb][i], sv = p_s[r], sg = p_sg[r];
+            p_u[r] = sv * b;
+            p_gb[r] = e * sv;
+            p_ga[r] = (e * b) * (fmaf(-sv, sg, sv) + sg);
+            if (r & 1) {  // slots r - 1 and r of the operands are complete
+              const int q = r >> 1;
+              gap[q] = pack_bf16x2(p_ga[r - 1], p_ga[r]);
+              gbp[q] = pack_bf16x2(p_gb[r - 1], p_gb[r]);
+              up[q] = pack_bf16x2(p_u[r - 1], p_u[r]);
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      stage(t + 2);
+      __syncthreads();
+      f = fn;
+      prev = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
+    }
+    if (ntiles > 1) {  // t = ntiles - 1: no forward
+      const Grad cur = pointwise(f);
+      backward(ntiles - 2, prev);
+      prev = cur;
+    }
+    backward(ntiles - 1, prev);
   }
 
   // Partial sums in natural weight layouts: [3][h*d] per (chunk, head).
