@@ -10,9 +10,9 @@
 //            U = SiLU(A) (*) B, written to LDS as bf16 [token][hidden];
 //   phase 2  each wave computes O^T = W2[Dw, :] U^T for its own output rows
 //            Dw (its W2 rows live in registers), K = all h hidden units.
-// Phase 1 of tile i and phase 2 of tile i-1 run between the same pair of
-// barriers, so the MFMA work of one phase overlaps the pointwise work of the
-// other.
+// The tiles are software-pipelined (see the main loop) so that MFMA work of
+// two tiles is interleaved with the gate's VALU / transcendental work of a
+// third.
 #include "zm_internal.h"
 
 namespace zm {
@@ -20,8 +20,11 @@ namespace zm {
 template <int D, int HID>
 struct AppCfg {
   static constexpr int T = kTok;
-  static constexpr int DP = D + 8;            // Q tile row pitch (elements)
-  static constexpr int UP = HID + 8;          // U tile row pitch
+  // Row pitches 32 bytes past a multiple of the 512-byte LDS bank period, so
+  // the 32 lanes served together by a 16-byte row read hit distinct banks.
+  static constexpr int DP = D + 16;           // Q tile row pitch (elements)
+  static constexpr int UP = HID + 16;         // U tile row pitch
+  static constexpr int OP = D + 16;           // output tile row pitch
   static constexpr int HPW = HID / kWaves;    // phase-1 hidden units per wave (16 or 32)
   static constexpr int MB1 = HPW / 16;        // phase-1 row blocks per wave
   static constexpr int KS1 = D / 32;          // phase-1 k-steps
@@ -37,9 +40,12 @@ struct AppCfg {
   static_assert(ITEMS <= kWaves * 64, "staging");
 };
 
-__device__ __forceinline__ float silu_gate(float a, float b) {
-  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
-  return a * sg * b;
+// SiLU(a) b up to the factor -log2(e): x = -log2(e) a comes out of the
+// matrix core (the bf16 W1 copy carries the factor) and the bf16 W2 copy
+// carries -1/log2(e), so x sig(a) b is what the second product needs.
+__device__ __forceinline__ float silu_gate(float x, float b) {
+  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
+  return x * sg * b;
 }
 
 template <int D, int HID>
@@ -52,6 +58,7 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
                 DB = C::DB, TBW = C::TBW, KS2 = C::KS2, CPT = C::CPT;
   __shared__ __attribute__((aligned(16))) uint16_t qs[2][T * DP];
   __shared__ __attribute__((aligned(16))) uint16_t us[2][T * UP];
+  __shared__ __attribute__((aligned(16))) uint16_t os[2][T * C::OP];
 
   const int head = blockIdx.x % heads;
   const int64_t t_begin = (int64_t)(blockIdx.x / heads) * chunk;
@@ -89,94 +96,232 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
 
   const bool has_item = tid < C::ITEMS;
   const int s_tok = tid / CPT, s_ch = tid - (tid / CPT) * CPT;
+  // Query rows past the end are fetched from a valid row (the tile's first)
+  // and their outputs are never stored, so no zeroing is needed.
+  const int lane_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
   u32x4 qr = {0u, 0u, 0u, 0u};
   auto fetch = [&](int it) {
-    qr = u32x4{0u, 0u, 0u, 0u};
-    const int64_t t = t_begin + (int64_t)it * T + s_tok;
-    if (has_item && t < t_end) qr = *(const u32x4*)(qp + t * ld + (int64_t)head * D + 8 * s_ch);
+    const int64_t t0 = t_begin + (int64_t)it * T;
+    if (t0 + T <= t_end) {
+      qr = *(const u32x4*)(qp + t0 * ld + lane_off);
+    } else {
+      const int64_t tc = (has_item && t0 < t_end && t0 + s_tok < t_end) ? t0 + s_tok
+                         : (t0 < t_end ? t0 : t_begin);
+      qr = *(const u32x4*)(qp + tc * ld + head * D + (has_item ? 8 * s_ch : 0));
+    }
   };
   auto stage = [&](int buf) {
-    if (has_item) *(u32x4*)(&qs[buf][s_tok * DP + 8 * s_ch]) = qr;
+    if constexpr (C::ITEMS < kWaves * 64) {
+      if (!has_item) return;
+    }
+    *(u32x4*)(&qs[buf & 1][s_tok * DP + 8 * s_ch]) = qr;
   };
 
-  auto phase1 = [&](int buf) {
-    f32x4 aa[MB1][NB], bb[MB1][NB];
+  struct Acc1 {
+    f32x4 a[MB1][NB], b[MB1][NB];
+  };
+  // phase-1 slot (ks, nb): one Q^T operand, 2 * MB1 MFMAs
+  auto p1_frag = [&](int buf, int ks, int nb) {
+    return as_bf16x8(*(const u32x4*)(&qs[buf & 1][(16 * nb + c) * DP + 32 * ks + 8 * g]));
+  };
+  auto p1_mma = [&](Acc1& x, int ks, int nb, const bf16x8& qf) {
 #pragma unroll
-    for (int mb = 0; mb < MB1; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        aa[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        bb[mb][nb] = aa[mb][nb];
+    for (int mb = 0; mb < MB1; ++mb) {
+      if (ks == 0) {
+        x.a[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        x.b[mb][nb] = x.a[mb][nb];
       }
-#pragma unroll
-    for (int ks = 0; ks < KS1; ++ks) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        // B = Q^T: lane holds Q[16 nb + c][32 ks + 8 g .. +7]
-        const bf16x8 qf = as_bf16x8(*(const u32x4*)(&qs[buf][(16 * nb + c) * DP + 32 * ks + 8 * g]));
-#pragma unroll
-        for (int mb = 0; mb < MB1; ++mb) {
-          aa[mb][nb] = mfma_bf16(w1f[mb][ks], qf, aa[mb][nb]);
-          bb[mb][nb] = mfma_bf16(w3f[mb][ks], qf, bb[mb][nb]);
-        }
-      }
+      x.a[mb][nb] = mfma_bf16(w1f[mb][ks], qf, x.a[mb][nb]);
+      x.b[mb][nb] = mfma_bf16(w3f[mb][ks], qf, x.b[mb][nb]);
     }
+  };
+  auto phase1 = [&](int buf) {
+    Acc1 x;
+#pragma unroll
+    for (int ks = 0; ks < KS1; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) p1_mma(x, ks, nb, p1_frag(buf, ks, nb));
+    return x;
+  };
+  // phase-2 slot (tbi, kp): two U^T operands (k-steps 2 kp, 2 kp + 1), 2 MFMAs
+  struct Frag2 {
+    bf16x8 x, y;
+  };
+  auto p2_frag = [&](int buf, int tbi, int kp) {
+    const uint16_t* row = &us[buf & 1][(16 * (tb0 + tbi) + c) * UP + 8 * g];
+    return Frag2{as_bf16x8(*(const u32x4*)(row + 64 * kp)),
+                 as_bf16x8(*(const u32x4*)(row + 64 * kp + 32))};
+  };
+  auto p2_mma = [&](f32x4* acc, int tbi, int kp, const Frag2& fr) {
+    if (kp == 0) acc[tbi] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[tbi] = mfma_bf16(w2f[2 * kp], fr.x, acc[tbi]);
+    acc[tbi] = mfma_bf16(w2f[2 * kp + 1], fr.y, acc[tbi]);
+  };
+  // Outputs go through LDS so that each output row leaves as one coalesced
+  // 16-byte-per-lane store: phase 2 of tile it writes its results (lane holds
+  // O[token 16 tb + c][16 db + 4 g + i]) into os[it % 2], and the next
+  // iteration, after the barrier, stores the tile to memory.
+  auto o_to_lds = [&](const f32x4* acc, int it) {
+#pragma unroll
+    for (int tbi = 0; tbi < TBW; ++tbi) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(acc[tbi][0], acc[tbi][1]);
+      pk[1] = pack_bf16x2(acc[tbi][2], acc[tbi][3]);
+      *(u32x2*)(&os[it & 1][(16 * (tb0 + tbi) + c) * C::OP + 16 * db + 4 * g]) = pk;
+    }
+  };
+  const int o_lane_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : 0;
+  auto o_from_lds = [&](int it) {
+    if constexpr (C::ITEMS < kWaves * 64) {
+      if (!has_item) return;
+    }
+    const int64_t tile0 = t_begin + (int64_t)it * T;
+    const u32x4 v = *(const u32x4*)(&os[it & 1][s_tok * C::OP + 8 * s_ch]);
+    if (tile0 + s_tok < t_end) *(u32x4*)(op + tile0 * ld + o_lane_off) = v;
+  };
+  // SiLU gate of element e (= (mb * NB + nb) * 4 + i) into the packed U rows
+  constexpr int NE = MB1 * NB * 4;
+  auto gate_elem = [&](const Acc1& x, int e, float* uv) {
+    const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
+    uv[e] = silu_gate(x.a[mb][nb][i], x.b[mb][nb][i]);
+  };
+  // U row nb of this wave: hidden j0 + 8 g .. (two row blocks) or j0 + 4 g ..
+  auto write_u = [&](int buf, const float* uv) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      uint16_t* dst = &us[buf][(16 * nb + c) * UP + j0];
+      uint16_t* dst = &us[buf & 1][(16 * nb + c) * UP + j0];
       if constexpr (MB1 == 2) {
         u32x4 pk;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-          pk[2 * mb] = pack_bf16x2(silu_gate(aa[mb][nb][0], bb[mb][nb][0]),
-                                   silu_gate(aa[mb][nb][1], bb[mb][nb][1]));
-          pk[2 * mb + 1] = pack_bf16x2(silu_gate(aa[mb][nb][2], bb[mb][nb][2]),
-                                       silu_gate(aa[mb][nb][3], bb[mb][nb][3]));
+          const int e0 = (mb * NB + nb) * 4;
+          pk[2 * mb] = pack_bf16x2(uv[e0], uv[e0 + 1]);
+          pk[2 * mb + 1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
         }
         *(u32x4*)(dst + 8 * g) = pk;
       } else {
+        const int e0 = nb * 4;
         u32x2 pk;
-        pk[0] = pack_bf16x2(silu_gate(aa[0][nb][0], bb[0][nb][0]), silu_gate(aa[0][nb][1], bb[0][nb][1]));
-        pk[1] = pack_bf16x2(silu_gate(aa[0][nb][2], bb[0][nb][2]), silu_gate(aa[0][nb][3], bb[0][nb][3]));
+        pk[0] = pack_bf16x2(uv[e0], uv[e0 + 1]);
+        pk[1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
         *(u32x2*)(dst + 4 * g) = pk;
       }
     }
   };
 
-  auto phase2 = [&](int buf, int it) {
-    const int64_t tile0 = t_begin + (int64_t)it * T;
-#pragma unroll
-    for (int tbi = 0; tbi < TBW; ++tbi) {
-      const int tb = tb0 + tbi;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS2; ++ks) {
-        // B = U^T: lane holds U[16 tb + c][32 ks + 8 g .. +7]
-        const bf16x8 uf = as_bf16x8(*(const u32x4*)(&us[buf][(16 * tb + c) * UP + 32 * ks + 8 * g]));
-        acc = mfma_bf16(w2f[ks], uf, acc);
-      }
-      // lane holds O[token 16 tb + c][16 db + 4 g + i]
-      const int64_t t = tile0 + 16 * tb + c;
-      if (t < t_end) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2(acc[0], acc[1]);
-        pk[1] = pack_bf16x2(acc[2], acc[3]);
-        *(u32x2*)(op + t * ld + (int64_t)head * D + 16 * db + 4 * g) = pk;
-      }
-    }
-  };
-
+  // Software pipeline: iteration i gates tile i (VALU), multiplies tile i - 1
+  // through W2 (phase 2) and tile i + 1 through W1, W3 (phase 1), as slots of
+  // MFMAs each preceded by the LDS fetch of the next slot and followed by one
+  // element of the gate work; then U(i) goes to LDS, O(i - 1) to memory and
+  // Q(i + 2) is staged.  Two Q and two U buffers; one barrier per iteration.
+  constexpr int NS2 = TBW * KS2 / 2;   // phase-2 slots
+  constexpr int NS1 = KS1 * NB;        // phase-1 slots
+  constexpr int NSLOT = NS1 + NS2;
   fetch(0);
   stage(0);
+  fetch(1);
+  stage(1);
   __syncthreads();
-  for (int it = 0; it <= ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
-    if (more) fetch(it + 1);
-    if (it < ntiles) phase1(it & 1);
-    if (it > 0) phase2((it - 1) & 1, it - 1);
-    if (more) stage((it + 1) & 1);
+  Acc1 cur = phase1(0);
+  __syncthreads();  // every wave is done with Q(0) before Q(2) reuses its buffer
+  f32x4 acc2[TBW];
+  {  // i = 0: no phase 2 yet
+    float uv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) gate_elem(cur, e, uv);
+    if (ntiles > 1) cur = phase1(1);
+    write_u(0, uv);
+    fetch(2);
+    stage(2);
     __syncthreads();
   }
+  // Slots alternate phase 2 (two MFMAs) and phase 1 (2 * MB1 MFMAs) while
+  // both last; the gate runs as a rolling three-stage pipeline over the
+  // elements: in slot j, exp2 for element j, reciprocal for j - 1 and the
+  // products for j - 2, so each slot holds independent work.
+  auto slot_is_p2 = [&](int j) {
+    constexpr int both = 2 * (NS1 < NS2 ? NS1 : NS2);
+    return j < both ? (j & 1) == 0 : NS2 > NS1;
+  };
+  auto slot_idx = [&](int j) {  // index within its phase
+    constexpr int both = 2 * (NS1 < NS2 ? NS1 : NS2);
+    return j < both ? (j >> 1) : (j - both / 2);
+  };
+  auto step = [&](int it, const Acc1& cur, Acc1& nxt) {
+    fetch(it + 2);
+    if (it >= 2) o_from_lds(it - 2);
+    float ev[NE], sv[NE], uv[NE];
+    Frag2 f2[NSLOT];
+    bf16x8 f1[NSLOT];
+    auto load_slot = [&](int j) {
+      const int k = slot_idx(j);
+      if (slot_is_p2(j)) f2[j] = p2_frag(it - 1, k / (KS2 / 2), k % (KS2 / 2));
+      else f1[j] = p1_frag(it + 1, k / NB, k % NB);
+    };
+    auto gate_a = [&](int e) {
+      const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
+      ev[e] = __builtin_amdgcn_exp2f(cur.a[mb][nb][i]);
+    };
+    auto gate_b = [&](int e) { sv[e] = __builtin_amdgcn_rcpf(1.f + ev[e]); };
+    auto gate_c = [&](int e) {
+      const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
+      uv[e] = cur.a[mb][nb][i] * sv[e] * cur.b[mb][nb][i];
+    };
+    load_slot(0);
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j + 1 < NSLOT) load_slot(j + 1);
+      const int k = slot_idx(j);
+      if (slot_is_p2(j)) p2_mma(acc2, k / (KS2 / 2), k % (KS2 / 2), f2[j]);
+      else p1_mma(nxt, k / NB, k % NB, f1[j]);
+      const int lo = (NE * j) / NSLOT, hi = (NE * (j + 1)) / NSLOT;
+#pragma unroll
+      for (int e = lo; e < hi; ++e) {
+        gate_a(e);
+        if (e >= 1) gate_b(e - 1);
+        if (e >= 2) gate_c(e - 2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    gate_b(NE - 1);
+    gate_c(NE - 2);
+    gate_c(NE - 1);
+    write_u(it, uv);
+    o_to_lds(acc2, it - 1);
+    stage(it + 2);
+    __syncthreads();
+  };
+  Acc1 alt;
+  int it = 1;
+  for (; it + 2 < ntiles; it += 2) {  // two steady iterations per trip
+    step(it, cur, alt);
+    step(it + 1, alt, cur);
+  }
+  if (it + 1 < ntiles) {
+    step(it, cur, alt);
+    cur = alt;
+  }
+  if (ntiles > 1) {  // i = ntiles - 1: no phase 1
+    if (ntiles >= 3) o_from_lds(ntiles - 3);
+    float uv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) gate_elem(cur, e, uv);
+#pragma unroll
+    for (int tbi = 0; tbi < TBW; ++tbi)
+#pragma unroll
+      for (int kp = 0; kp < KS2 / 2; ++kp) p2_mma(acc2, tbi, kp, p2_frag(ntiles - 2, tbi, kp));
+    write_u(ntiles - 1, uv);
+    o_to_lds(acc2, ntiles - 2);
+    __syncthreads();
+    o_from_lds(ntiles - 2);
+  }
+#pragma unroll
+  for (int tbi = 0; tbi < TBW; ++tbi)
+#pragma unroll
+    for (int kp = 0; kp < KS2 / 2; ++kp) p2_mma(acc2, tbi, kp, p2_frag(ntiles - 1, tbi, kp));
+  o_to_lds(acc2, ntiles - 1);
+  __syncthreads();
+  o_from_lds(ntiles - 1);
 }
 
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,

@@ -32,20 +32,6 @@
 // fixed order (no atomics, bitwise reproducible).
 #include "zm_internal.h"
 
-// Schedule knobs of the steady-state loop (compile-time; defaults are the
-// measured best): LDS fetch lookahead in slots, slot order (0: all backward
-// slots then all forward slots; 1: alternating), and whether MFMA issue
-// runs at raised wave priority.
-#ifndef ZM_LOOKAHEAD
-#define ZM_LOOKAHEAD 1
-#endif
-#ifndef ZM_ORDER
-#define ZM_ORDER 0
-#endif
-#ifndef ZM_PRIO
-#define ZM_PRIO 0
-#endif
-
 namespace zm {
 
 template <int D, int HID>
@@ -60,12 +46,13 @@ struct UpdCfg {
   static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
 };
 
-// Tile layout: row r (token) of D bf16, 16-byte chunk ch stored at chunk
-// ch ^ swz(r).  With the token map tau, the 16 rows one forward read touches
-// and the 8 rows one half-wave transposing read touches fall in distinct banks.
+// Tile layout: row r (token) of D bf16 (no padding), 16-byte chunk ch
+// stored at chunk ch ^ swz(r).  With the token map tau below, the 16 rows one
+// forward read touches and the 8 rows one half-wave transposing read touches
+// start in distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  constexpr int half = D / 16;                  // chunks per row / 2
+  constexpr int half = D / 16;  // chunks per row / 2
   constexpr int sh = D == 128 ? 0 : 1;
   return 2 * ((r >> sh) & (half - 1)) + ((r >> 4) & 1);
 }
@@ -73,7 +60,8 @@ template <int D>
 __device__ __forceinline__ int tile_off(int r, int col) {  // col multiple of 4
   return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
 }
-// Token held in operand slot j (0..7) by the lanes of 16-lane group g.
+// Token held in operand slot j (0..7) by the lanes of 16-lane group g; the
+// forward's MFMA row m = 4 g' + i of block mb reads token tau(g', 4 mb + i).
 __device__ __forceinline__ int tau(int g, int j) {
   return 16 * (g >> 1) + 4 * (g & 1) + 8 * (j >> 2) + (j & 3);
 }
@@ -86,16 +74,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
       (lds_bf16x4*)((__attribute__((address_space(3))) void*)(p)));
 }
 
-// SiLU / gate backward for one (token, hidden) element.  a = W1 k, b = W3 k,
-// e = W2^T (eta v).  Returns ga, gb and u = SiLU(a) b.
-__device__ __forceinline__ void gate_backward(float a, float b, float e, float& ga, float& gb,
+// SiLU / gate backward for one (token, hidden) element.  x = -log2(e) W1 k
+// (the bf16 W1 copy carries the factor), b = W3 k, e = W2^T (eta v).
+// Returns ga and, scaled by -log2(e), gb and u = SiLU(a) b; the kernel undoes
+// that scale on the dW3 and dW2 partial sums.  With s' = x sig:
+//   sig = 1 / (1 + 2^x),  s = SiLU(a) = -s' / log2(e),
+//   ga = e b (sig + s (1 - sig)),  gb' = e s',  u' = s' b.
+__device__ __forceinline__ void gate_backward(float x, float b, float e, float& ga, float& gb,
                                               float& u) {
-  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
-  const float s = a * sg;
-  u = s * b;
-  gb = e * s;
-  const float dsilu = fmaf(-s, sg, s) + sg;  // sig + s (1 - sig)
-  ga = (e * b) * dsilu;
+  const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
+  const float sp = x * sg;
+  u = sp * b;
+  gb = e * sp;
+  ga = (e * b) * fmaf(fmaf(-sp, sg, sp), kNegInvLog2e, sg);
 }
 
 template <int D, int HID>
@@ -161,11 +152,13 @@ __global__ __launch_bounds__(512) void k_update_bf16(
       vr = *(const u32x4*)(vp + t0 * ld + lane_tok_off);
       er = eta[t0 * heads + lane_eta_off];
     } else {
-      // Tail tile: out-of-range tokens get eta = 0 and the tile's first
-      // token's k and v (finite values; eta = 0 zeroes their contribution,
-      // since e, ga, gb and V_eta all carry eta).
+      // Tail tile: out-of-range tokens get eta = 0 and a real token's k and v
+      // (finite values; eta = 0 zeroes their contribution, since e, ga, gb
+      // and V_eta all carry eta).
+      // Tiles past the last one (prefetch overrun) read the chunk's first
+      // token, so every load stays inside the token array.
       const bool ok = has_item && t0 + s_tok < t_end;
-      const int64_t tc = ok ? t0 + s_tok : t0;
+      const int64_t tc = ok ? t0 + s_tok : (t0 < t_end ? t0 : t_begin);
       const int col = has_item ? 8 * s_ch : 0;
       kr = *(const u32x4*)(kp + tc * ld + head * D + col);
       vr = *(const u32x4*)(vp + tc * ld + head * D + col);
@@ -293,100 +286,114 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   };
 
   // Software pipeline over tiles, four LDS buffers (tile t in buffer t % 4).
-  // Iteration t (steady state) is 16 slots: backward(t - 1) in slots 0..7 and
-  // forward(t + 1) in slots 8..15, each slot's LDS fetch issued two slots
-  // ahead; the pointwise backward of tile t is spread over the slots (half of
-  // one element row per slot) so its VALU and transcendental work runs while
-  // the MFMAs of the same wave are in flight.  Staging of tile t + 2 and one
-  // barrier close the iteration.  The fences keep this order through the
-  // compiler's scheduler.
+  // Steady-state iteration t is 16 slots: backward(t - 1) in slots 0..7 and
+  // forward(t + 1) in slots 8..15, each slot's LDS fetch issued one slot
+  // ahead.  The pointwise backward of tile t runs beside them as a rolling
+  // pipeline over its 8 element rows: even slot 2k computes the exp2 of row k
+  // and the gradient products of row k - 1, odd slot 2k + 1 the sigmoid of
+  // row k.  Staging of tile t + 2 and one barrier close the iteration.  The
+  // fences keep this order through the compiler's scheduler, and the loop is
+  // unrolled by two so the carried state alternates between two register
+  // sets instead of being copied.
+  constexpr int NBS = MB;            // backward slots
+  constexpr int NSLOT = NBS + 2 * KS;
+  auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur) {
+    fetch(t + 2);
+    float p_s[8], p_sg[8], p_ga[8], p_gb[8], p_u[8];
+    u32x4 gap, gbp, up;
+    auto load_slot = [&](int j) {
+      return j < NBS ? bwd_frag(t - 1, j) : fwd_frag(t + 1, (j - NBS) / KS, (j - NBS) % KS);
+    };
+    auto sig_row = [&](int r) {  // sigmoid and s' of element row r (after its exp2)
+      const float sg = __builtin_amdgcn_rcpf(1.f + p_sg[r]);
+      p_sg[r] = sg;
+      p_s[r] = f.a[r >> 2][r & 3] * sg;
+    };
+    auto grad_row = [&](int r) {  // gradient products of row r, packed per pair
+      const int mb = r >> 2, i = r & 3;
+      const float b = f.b[mb][i], e = f.e[mb][i], sp = p_s[r], sg = p_sg[r];
+      p_u[r] = sp * b;
+      p_gb[r] = e * sp;
+      p_ga[r] = (e * b) * fmaf(fmaf(-sp, sg, sp), kNegInvLog2e, sg);
+      if (r & 1) {
+        const int q = r >> 1;
+        gap[q] = pack_bf16x2(p_ga[r - 1], p_ga[r]);
+        gbp[q] = pack_bf16x2(p_gb[r - 1], p_gb[r]);
+        up[q] = pack_bf16x2(p_u[r - 1], p_u[r]);
+      }
+    };
+    Frag2 fr[NSLOT];
+    fr[0] = load_slot(0);
+#pragma unroll
+    for (int j = 0; j < NSLOT; ++j) {
+      if (j + 1 < NSLOT) fr[j + 1] = load_slot(j + 1);
+      if (j < NBS) {
+        bwd_mma(j, fr[j], prev);
+      } else {
+        const int mb = (j - NBS) / KS, ks = (j - NBS) % KS;
+        if (ks == 0) {  // first k-step: start from zero accumulators
+          fn.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          fn.b[mb] = fn.a[mb];
+          fn.e[mb] = fn.a[mb];
+        }
+        fwd_mma(fn, mb, ks, fr[j]);
+      }
+      // element rows of the pointwise handled in this slot (16 half-rows
+      // spread over NSLOT slots): even half h = 2r is exp2, odd half the rest
+#pragma unroll
+      for (int h = (16 * j) / NSLOT; h < (16 * (j + 1)) / NSLOT; ++h) {
+        const int rr = h >> 1;
+        if ((h & 1) == 0) {
+          p_sg[rr] = __builtin_amdgcn_exp2f(f.a[rr >> 2][rr & 3]);
+          if (rr >= 1) grad_row(rr - 1);
+        } else {
+          sig_row(rr);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    grad_row(7);
+    stage(t + 2);
+    __syncthreads();
+    cur = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
+  };
+
   if (ntiles > 0) {
     fetch(0);
     stage(0);
     fetch(1);
     stage(1);
     __syncthreads();
-    Fwd f = forward(0);
-    Grad prev;
-    {  // t = 0: no backward yet
-      fetch(2);
-      const Grad cur = pointwise(f);
-      if (ntiles > 1) f = forward(1);
-      stage(2);
-      __syncthreads();
-      prev = cur;
+    Fwd fa = forward(0), fb;
+    Grad ga_ = pointwise(fa), gb_;
+    // t = 0: no backward yet
+    fetch(2);
+    if (ntiles > 1) fa = forward(1);
+    stage(2);
+    __syncthreads();
+    int t = 1;
+    for (; t + 2 < ntiles; t += 2) {  // steady state, two iterations per trip
+      step(t, fa, ga_, fb, gb_);
+      step(t + 1, fb, gb_, fa, ga_);
     }
-    constexpr int NB = MB;            // backward slots
-    constexpr int NF = 2 * KS;        // forward slots
-    constexpr int NSLOT = NB + NF;
-    for (int t = 1; t + 1 < ntiles; ++t) {  // steady state
-      fetch(t + 2);
-      Fwd fn;
-      float p_s[8], p_sg[8], p_ga[8], p_gb[8], p_u[8];
-      u32x4 gap, gbp, up;
-      // Slot j runs backward block bslot(j) or forward step fslot(j).
-      auto is_bwd = [&](int j) { return ZM_ORDER == 0 ? j < NB : (j & 1) == 0; };
-      auto bidx = [&](int j) { return ZM_ORDER == 0 ? j : j >> 1; };
-      auto fidx = [&](int j) { return ZM_ORDER == 0 ? j - NB : j >> 1; };
-      auto load_slot = [&](int j) {
-        return is_bwd(j) ? bwd_frag(t - 1, bidx(j)) : fwd_frag(t + 1, fidx(j) / KS, fidx(j) % KS);
-      };
-      Frag2 fr[NSLOT];
-#pragma unroll
-      for (int j = 0; j < ZM_LOOKAHEAD; ++j) fr[j] = load_slot(j);
-#pragma unroll
-      for (int j = 0; j < NSLOT; ++j) {
-        if (j + ZM_LOOKAHEAD < NSLOT) fr[j + ZM_LOOKAHEAD] = load_slot(j + ZM_LOOKAHEAD);
-        if (ZM_PRIO) __builtin_amdgcn_s_setprio(1);
-        if (is_bwd(j)) {
-          bwd_mma(bidx(j), fr[j], prev);
-        } else {
-          const int mb = fidx(j) / KS, ks = fidx(j) % KS;
-          if (ks == 0) {  // first k-step: start from zero accumulators
-            fn.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            fn.b[mb] = fn.a[mb];
-            fn.e[mb] = fn.a[mb];
-          }
-          fwd_mma(fn, mb, ks, fr[j]);
-        }
-        if (ZM_PRIO) __builtin_amdgcn_s_setprio(0);
-        // Each slot does the pointwise halves h in [16 j / NSLOT, 16 (j + 1) / NSLOT):
-        // even h: sigmoid and SiLU of element row h / 2; odd h: its gradients.
-#pragma unroll
-        for (int h = (16 * j) / NSLOT; h < (16 * (j + 1)) / NSLOT; ++h) {
-          const int r = h >> 1, mb = r >> 2, i = r & 3;
-          if ((h & 1) == 0) {
-            const float a = f.a[mb][i];
-            const float sg = __builtin_amdgcn_rcpf(
-                1.f + __builtin_amdgcn_exp2f(-1.44269504088896341f * a));
-            p_sg[r] = sg;
-            p_s[r] = a * sg;
-          } else {
-            const float b = f.b[mb][i], e = f.e[mb][i], sv = p_s[r], sg = p_sg[r];
-            p_u[r] = sv * b;
-            p_gb[r] = e * sv;
-            p_ga[r] = (e * b) * (fmaf(-sv, sg, sv) + sg);
-            if (r & 1) {  // slots r - 1 and r of the operands are complete
-              const int q = r >> 1;
-              gap[q] = pack_bf16x2(p_ga[r - 1], p_ga[r]);
-              gbp[q] = pack_bf16x2(p_gb[r - 1], p_gb[r]);
-              up[q] = pack_bf16x2(p_u[r - 1], p_u[r]);
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      stage(t + 2);
-      __syncthreads();
-      f = fn;
-      prev = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
+    if (t + 1 < ntiles) {  // one steady iteration left
+      step(t, fa, ga_, fb, gb_);
+      fa = fb;
+      ga_ = gb_;
+      ++t;
     }
     if (ntiles > 1) {  // t = ntiles - 1: no forward
-      const Grad cur = pointwise(f);
-      backward(ntiles - 2, prev);
-      prev = cur;
+      const Grad cur = pointwise(fa);
+      backward(ntiles - 2, ga_);
+      ga_ = cur;
     }
-    backward(ntiles - 1, prev);
+    backward(ntiles - 1, ga_);
+  }
+  // dW3 and dW2 were accumulated from gb' and u', which carry -log2(e)
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    acc3[m] *= kNegInvLog2e;
+    acc2[m] *= kNegInvLog2e;
   }
 
   // Partial sums in natural weight layouts: [3][h*d] per (chunk, head).

@@ -19,9 +19,9 @@ __global__ __launch_bounds__(256) void k_cast(const float* __restrict__ w1,
   const int64_t total = (int64_t)heads * h * d;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  out.w1b[i] = to_bf16(w1[i]);
+  out.w1b[i] = to_bf16(kNegLog2e * w1[i]);
   out.w3b[i] = to_bf16(w3[i]);
-  out.w2b[i] = to_bf16(w2[i]);  // same element count, [H][d][h] order
+  out.w2b[i] = to_bf16(kNegInvLog2e * w2[i]);  // same element count, [H][d][h] order
   const int64_t hd = i / ((int64_t)h * d);
   const int64_t rem = i - hd * h * d;
   const int64_t j = rem / d, c = rem - j * d;
@@ -108,14 +108,13 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
       const int col = lane + 64 * e;
       wout[base + col] = nv[e];
       if (emit_bf16) {
-        const uint16_t bv = to_bf16(nv[e]);
         if (mat == 0) {
-          ob.w1b[base + col] = bv;
+          ob.w1b[base + col] = to_bf16(kNegLog2e * nv[e]);
         } else if (mat == 1) {
-          ob.w3b[base + col] = bv;
+          ob.w3b[base + col] = to_bf16(nv[e]);
         } else {
-          ob.w2b[base + col] = bv;
-          ob.w2tb[((int64_t)head * h + col) * d + row] = bv;
+          ob.w2b[base + col] = to_bf16(kNegInvLog2e * nv[e]);
+          ob.w2tb[((int64_t)head * h + col) * d + row] = to_bf16(nv[e]);
         }
       }
     }

@@ -23,11 +23,17 @@ constexpr int kHidPerWgF32 = 64;  // hidden units owned by one fp32 update workg
 constexpr int kTargetWgs = 256;   // MI355X compute units: one workgroup each
 constexpr int kMinTilesPerChunk = 4;
 
-// bf16 copies of one weight set, [H][h][d] except w2b [H][d][h].
+// bf16 operand copies of one weight set, [H][h][d] except w2b [H][d][h].
+// Two copies carry a constant so that the kernels save a multiply per
+// (token, hidden unit): W1 is stored times -log2(e), so W1 x comes out of the
+// matrix core as the exponent of the sigmoid's exp2, and the apply's W2 is
+// stored times -1/log2(e) to undo that factor in SiLU(a) = a sig(a).
+constexpr float kNegLog2e = -1.44269504088896341f;
+constexpr float kNegInvLog2e = -0.693147180559945309f;
 struct WSet {
-  uint16_t* w1b;   // W1 rows (hidden-major)
+  uint16_t* w1b;   // -log2(e) W1 rows (hidden-major)
   uint16_t* w3b;   // W3 rows
-  uint16_t* w2b;   // W2 as stored: [d][h]
+  uint16_t* w2b;   // -W2 / log2(e), as stored: [d][h]
   uint16_t* w2tb;  // W2 transposed: [h][d]
 };
 
