@@ -44,7 +44,7 @@ def parse():
     p.add_argument("--workload", default="f700",
                    choices=["f700", "f100", "f8", "f700x24", "stream256"])
     p.add_argument("--seed", type=int, default=4)
-    p.add_argument("--cpu-sample-tokens", type=int, default=32768)
+    p.add_argument("--cpu-sample-tokens", type=int, default=262144)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-renorm", action="store_true")
     p.add_argument("--copy-calibration-mib", type=int, default=0,

@@ -271,13 +271,18 @@ def test_bitwise_determinism(io):
     assert torch.equal(oa, ob)
 
 
-def test_f700_full_size_sampled():
+@pytest.mark.parametrize("layer", [0, 23])
+def test_f700_full_size_sampled(layer):
     """The 700-frame workload in the launch configuration the benchmark
-    times, checked on sampled rows of W_hat and sampled query outputs."""
+    times (layer 23: the last layer of the 24-layer stack, fresh weights),
+    checked on sampled rows of W_hat and sampled query outputs."""
     wl = WL.WORKLOADS["f700"]
-    say("case f700 full size seed=4 (sampled checks)")
+    say(f"case f700 full size seed=4 layer={layer} (sampled checks)")
     inp = Inputs(wl, 4)
     t = inp.t
+    if layer:
+        t["w1"], t["w2"], t["w3"] = WL.make_weights(wl.heads, wl.d_head, wl.d_hidden, 4, "cuda",
+                                                    layer=layer)
     (g1, g2, g3), og = zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"],
                                        t["w3"], renorm=True)
     (f1, f2, f3), _ = zm.update_apply(t["k"], t["v"], t["eta"], t["q"][:0], t["w1"], t["w2"],
@@ -313,3 +318,46 @@ def test_f700_full_size_sampled():
     # the last tile of the chunk too
     ref = oracle.apply(host(t["q"][-40:]), host(g1), host(g2), host(g3))
     check("O last 40 queries", host(og[-40:]), ref, TOL["bf16"])
+
+
+def test_stream256_full_size_per_step():
+    """256 frames fed one at a time (the streaming workload the benchmark
+    times).  At sampled frames t the GPU's own state W(t-1) is taken as the
+    start: the frame's output must be f_{W(t-1)}(q_t) and the state step
+    W(t) - W(t-1) must match the oracle's step from W(t-1).  The first four
+    frames are also checked as a chain from W(0)."""
+    wl = WL.WORKLOADS["stream256"]
+    say("case stream256 full size seed=5 (per-step checks)")
+    inp = Inputs(wl, 5)
+    t = inp.t
+    w = [t["w1"].clone(), t["w2"].clone(), t["w3"].clone()]
+    sampled = {0, 1, 3, 128, 255}
+    before, after, outs = {}, {}, {}
+    slices = WL.frame_slices(wl)
+    for i, (s, e) in enumerate(slices):
+        if i in sampled:
+            before[i] = [host(x) for x in w]
+        o = zm.stream_step(t["q"][s:e], t["k"][s:e], t["v"][s:e], t["eta"][s:e], *w, renorm=True)
+        if i in sampled:
+            torch.cuda.synchronize()
+            after[i] = [host(x) for x in w]
+            outs[i] = host(o)
+    torch.cuda.synchronize()
+    assert all(torch.isfinite(x).all() for x in w)
+    for i in sorted(sampled):
+        s, e = slices[i]
+        wp = before[i]
+        ref_o = oracle.apply(host(t["q"][s:e]), *wp)
+        check(f"frame {i} O", outs[i], ref_o, TOL["bf16"])
+        ref_w = oracle.update(host(t["k"][s:e]), host(t["v"][s:e]), host(t["eta"][s:e]), *wp,
+                              renorm=True)
+        for nm, a, b, w0 in zip(("W1", "W2", "W3"), after[i], ref_w, wp):
+            check(f"frame {i} step {nm}", a - w0, b - w0, TOL["bf16"])
+    # chain of the first frames from the initial state
+    frames = [dict(q=host(t["q"][s:e]), k=host(t["k"][s:e]), v=host(t["v"][s:e]),
+                   eta=host(t["eta"][s:e])) for (s, e) in slices[:4]]
+    rw, routs = oracle.stream(frames, inp.np("w1"), inp.np("w2"), inp.np("w3"), renorm=True)
+    check("frame 0 O (chain)", outs[0], routs[0], TOL["bf16"])
+    check("frame 3 O (chain)", outs[3], routs[3], TOL["bf16"])
+    for nm, a, b in zip(("W1", "W2", "W3"), after[3], rw):
+        check(f"{nm} after 4 frames (chain)", a, b, TOL["bf16"])
