@@ -20,11 +20,18 @@ namespace zm {
 template <int D, int HID>
 struct AppCfg {
   static constexpr int T = kTok;
-  // Row pitches 32 bytes past a multiple of the 512-byte LDS bank period, so
-  // the 32 lanes served together by a 16-byte row read hit distinct banks.
+  // LDS layouts, each free of bank conflicts on gfx950 (64 four-byte banks
+  // for reads: a 16-byte read serves 16 lanes per cycle, grouped by half-wave
+  // and by the parity of the lane's quad index, an 8-byte read 32 lanes;
+  // writes go 128 bytes per cycle):
+  //   Q tile: rows padded by 32 bytes (row reads, 16-byte staging writes);
+  //   U tile: unpadded rows, 16-byte chunk ch of row r stored at ch ^ (r % 16)
+  //           (16-byte writes of 8 rows, row reads of 16 rows);
+  //   O tile: rows padded by 8 bytes, so the 8-byte writes of 16 rows and the
+  //           8-byte reads of the store both spread over all banks.
   static constexpr int DP = D + 16;           // Q tile row pitch (elements)
-  static constexpr int UP = HID + 16;         // U tile row pitch
-  static constexpr int OP = D + 16;           // output tile row pitch
+  static constexpr int UP = HID;              // U tile row pitch
+  static constexpr int OP = D + 4;            // output tile row pitch
   static constexpr int HPW = HID / kWaves;    // phase-1 hidden units per wave (16 or 32)
   static constexpr int MB1 = HPW / 16;        // phase-1 row blocks per wave
   static constexpr int KS1 = D / 32;          // phase-1 k-steps
@@ -46,6 +53,12 @@ struct AppCfg {
 __device__ __forceinline__ float silu_gate(float x, float b) {
   const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
   return x * sg * b;
+}
+
+// Element offset of U(r, col) in its tile (col a multiple of 4).
+template <int HID>
+__device__ __forceinline__ int u_off(int r, int col) {
+  return r * HID + (((col >> 3) ^ (r & 15)) << 3) + (col & 7);
 }
 
 template <int D, int HID>
@@ -148,9 +161,10 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     bf16x8 x, y;
   };
   auto p2_frag = [&](int buf, int tbi, int kp) {
-    const uint16_t* row = &us[buf & 1][(16 * (tb0 + tbi) + c) * UP + 8 * g];
-    return Frag2{as_bf16x8(*(const u32x4*)(row + 64 * kp)),
-                 as_bf16x8(*(const u32x4*)(row + 64 * kp + 32))};
+    const uint16_t* ub = us[buf & 1];
+    const int r = 16 * (tb0 + tbi) + c;
+    return Frag2{as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * kp))),
+                 as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * kp + 32)))};
   };
   auto p2_mma = [&](f32x4* acc, int tbi, int kp, const Frag2& fr) {
     if (kp == 0) acc[tbi] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -176,7 +190,9 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
       if (!has_item) return;
     }
     const int64_t tile0 = t_begin + (int64_t)it * T;
-    const u32x4 v = *(const u32x4*)(&os[it & 1][s_tok * C::OP + 8 * s_ch]);
+    const uint16_t* src = &os[it & 1][s_tok * C::OP + 8 * s_ch];
+    const u32x2 lo = *(const u32x2*)(src), hi = *(const u32x2*)(src + 4);
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
     if (tile0 + s_tok < t_end) *(u32x4*)(op + tile0 * ld + o_lane_off) = v;
   };
   // SiLU gate of element e (= (mb * NB + nb) * 4 + i) into the packed U rows
@@ -189,7 +205,8 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
   auto write_u = [&](int buf, const float* uv) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      uint16_t* dst = &us[buf & 1][(16 * nb + c) * UP + j0];
+      uint16_t* ub = us[buf & 1];
+      const int r = 16 * nb + c;
       if constexpr (MB1 == 2) {
         u32x4 pk;
 #pragma unroll
@@ -198,13 +215,13 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
           pk[2 * mb] = pack_bf16x2(uv[e0], uv[e0 + 1]);
           pk[2 * mb + 1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
         }
-        *(u32x4*)(dst + 8 * g) = pk;
+        *(u32x4*)(ub + u_off<HID>(r, j0 + 8 * g)) = pk;
       } else {
         const int e0 = nb * 4;
         u32x2 pk;
         pk[0] = pack_bf16x2(uv[e0], uv[e0 + 1]);
         pk[1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
-        *(u32x2*)(dst + 4 * g) = pk;
+        *(u32x2*)(ub + u_off<HID>(r, j0 + 4 * g)) = pk;
       }
     }
   };
