@@ -42,25 +42,26 @@ struct UpdCfg {
   static constexpr int MB = D / 16;             // 16-row blocks along d
   static constexpr int CPT = D / 8;             // 16-byte chunks per token row
   static constexpr int ITEMS = T * CPT;         // staging items per tile
-  static constexpr int BUF = 2 * T * D;         // elements per LDS buffer (K tile, V_eta tile)
+  static constexpr int TILE = T * (D + 16);      // elements per padded tile
+  static constexpr int BUF = 2 * TILE;           // elements per LDS buffer (K tile, V_eta tile)
   static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
 };
 
-// Tile layout: row r (token) of D bf16 (no padding), 16-byte chunk ch
-// stored at chunk ch ^ swz(r).  gfx950 LDS reads see 64 four-byte banks; a
-// 16-byte read is served 16 lanes per cycle (each half-wave split by the
-// parity of the lane's quad index), an 8-byte read 32 lanes per cycle, and
-// writes 128 bytes per cycle.  With the token map tau below, the forward row
-// reads, the transposing reads and the staging writes are all free of bank
-// conflicts: rows r and r + 16 share a swizzle, and the forward's lane groups
-// pair each of them with the other's neighbouring chunk.
+// Tile layout: row r (token) of D bf16, rows padded by 32 bytes.  gfx950 LDS
+// reads see 64 four-byte banks; a 16-byte read is served 16 lanes per cycle
+// (each half-wave split by the parity of the lane's quad index), an 8-byte
+// read 32 lanes per cycle, and writes go 128 bytes per cycle.  With this
+// pitch and the token map tau below, the forward row reads, the transposing
+// reads and the staging writes are all free of bank conflicts, and every
+// operand address of a slot is a per-lane base plus a constant, so the
+// addresses cost no VALU work inside the loop.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
-  return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+__device__ __forceinline__ constexpr int tile_pitch() {
+  return D + 16;
 }
 template <int D>
-__device__ __forceinline__ int tile_off(int r, int col) {  // col multiple of 4
-  return r * D + (((col >> 3) ^ swz<D>(r)) << 3) + (col & 7);
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * tile_pitch<D>() + col;
 }
 // Token held in operand slot j (0..7) by the lanes of 16-lane group g; the
 // forward's MFMA row m = 4 g' + i of block mb reads token tau(g', 4 mb + i).
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
       if (!has_item) return;
     }
     uint16_t* ktm = lds + (buf & 3) * C::BUF;
-    uint16_t* vtm = ktm + T * D;
+    uint16_t* vtm = ktm + C::TILE;
     u32x4 vs;
 #pragma unroll
     for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(vr[q]) * er, bf16hi(vr[q]) * er);
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
 
   // Transposing-read addresses: lane (g, s) loads 4 columns 16 m + 4 (s % 4)
   // of rows tau(g, s / 4) (slots 0..3) and tau(g, 4 + s / 4) (slots 4..7).
-  const int row_a = tau(g, c >> 2), row_b = row_a + 8;  // swz(row_b) == swz(row_a)
+  const int row_a = tau(g, c >> 2), row_b = row_a + 8;
 
   struct Fwd {
     f32x4 a[2], b[2], e[2];
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   // forward A = K W1^T, B = K W3^T, E = V_eta W2 on one tile (24 MFMAs)
   auto forward = [&](int buf) {
     const uint16_t* ktm = lds + (buf & 3) * C::BUF;
-    const uint16_t* vtm = ktm + T * D;
+    const uint16_t* vtm = ktm + C::TILE;
     Fwd f;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   // backward D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta (24 MFMAs)
   auto backward = [&](int buf, const Grad& gr) {
     const uint16_t* ktm = lds + (buf & 3) * C::BUF;
-    const uint16_t* vtm = ktm + T * D;
+    const uint16_t* vtm = ktm + C::TILE;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       const int col = 16 * m + 4 * (c & 3);
@@ -265,7 +266,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const uint16_t* ktm = lds + (buf & 3) * C::BUF;
     const int off = tile_off<D>(tau(c >> 2, 4 * mb + (c & 3)), 32 * ks + 8 * g);
     return Frag2{as_bf16x8(*(const u32x4*)(ktm + off)),
-                 as_bf16x8(*(const u32x4*)(ktm + T * D + off))};
+                 as_bf16x8(*(const u32x4*)(ktm + C::TILE + off))};
   };
   auto fwd_mma = [&](Fwd& f, int mb, int ks, const Frag2& fr) {
     f.a[mb] = mfma_bf16(fr.x, w1f[ks], f.a[mb]);
@@ -278,8 +279,8 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const int oa = tile_off<D>(row_a, col), ob = tile_off<D>(row_b, col);
     return Frag2{__builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
                                          0, 1, 2, 3, 4, 5, 6, 7),
-                 __builtin_shufflevector(lds_read_tr(ktm + T * D + oa),
-                                         lds_read_tr(ktm + T * D + ob), 0, 1, 2, 3, 4, 5, 6, 7)};
+                 __builtin_shufflevector(lds_read_tr(ktm + C::TILE + oa),
+                                         lds_read_tr(ktm + C::TILE + ob), 0, 1, 2, 3, 4, 5, 6, 7)};
   };
   auto bwd_mma = [&](int m, const Frag2& fr, const Grad& gr) {
     acc1[m] = mfma_bf16(fr.x, gr.ga, acc1[m]);
@@ -287,74 +288,126 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     acc2[m] = mfma_bf16(gr.u, fr.y, acc2[m]);
   };
 
-  // Software pipeline over tiles, four LDS buffers (tile t in buffer t % 4).
-  // Steady-state iteration t is 16 slots: backward(t - 1) in slots 0..7 and
-  // forward(t + 1) in slots 8..15, each slot's LDS fetch issued one slot
-  // ahead.  The pointwise backward of tile t runs beside them as a rolling
-  // pipeline over its 8 element rows: even slot 2k computes the exp2 of row k
-  // and the gradient products of row k - 1, odd slot 2k + 1 the sigmoid of
-  // row k.  Staging of tile t + 2 and one barrier close the iteration.  The
-  // fences keep this order through the compiler's scheduler, and the loop is
-  // unrolled by two so the carried state alternates between two register
-  // sets instead of being copied.
   constexpr int NBS = MB;            // backward slots
   constexpr int NSLOT = NBS + 2 * KS;
-  auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur) {
+  constexpr int LA = 1;              // LDS operand lookahead, in slots (2 spills)
+  auto load_slot = [&](int t, int j) __attribute__((always_inline)) {
+    return j < NBS ? bwd_frag(t - 1, j) : fwd_frag(t + 1, (j - NBS) / KS, (j - NBS) % KS);
+  };
+  // Steady iteration t: backward(t - 1) in slots 0..NBS-1 and forward(t + 1)
+  // in slots NBS..NSLOT-1, three MFMAs per slot, each slot's LDS operands
+  // fetched LA slots ahead.  The gate backward of tile t is cut into
+  // micro-steps of at most two plain VALU operations or one transcendental,
+  // and one micro-step follows each MFMA: on gfx950 about that much VALU work
+  // issues in the shadow of a 16x16x32 MFMA, while longer VALU runs stall
+  // the matrix core.  Element rows are processed in pairs (two independent
+  // chains), 14 micro-steps per pair; the steps left over after the last
+  // MFMA, then staging of tile t + 2 and one barrier close the iteration.
+  // Every gate value is pinned where it is computed so that the compiler
+  // keeps this placement.  The loop is unrolled by two so the carried state
+  // alternates between two register sets instead of being copied.
+  constexpr int NMICRO = 4 * 14;
+  auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur)
+      __attribute__((always_inline)) {
     fetch(t + 2);
-    float p_s[8], p_sg[8], p_ga[8], p_gb[8], p_u[8];
+    Frag2 fr[NSLOT];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) fr[j] = load_slot(t, j);
+    float g_t[2], g_sg[2], g_sp[2], g_u[2], g_gb[2], g_w[2], g_eb[2], g_ga[2];
     u32x4 gap, gbp, up;
-    auto load_slot = [&](int j) {
-      return j < NBS ? bwd_frag(t - 1, j) : fwd_frag(t + 1, (j - NBS) / KS, (j - NBS) % KS);
-    };
-    auto sig_row = [&](int r) {  // sigmoid and s' of element row r (after its exp2)
-      const float sg = __builtin_amdgcn_rcpf(1.f + p_sg[r]);
-      p_sg[r] = sg;
-      p_s[r] = f.a[r >> 2][r & 3] * sg;
-    };
-    auto grad_row = [&](int r) {  // gradient products of row r, packed per pair
-      const int mb = r >> 2, i = r & 3;
-      const float b = f.b[mb][i], e = f.e[mb][i], sp = p_s[r], sg = p_sg[r];
-      p_u[r] = sp * b;
-      p_gb[r] = e * sp;
-      p_ga[r] = (e * b) * fmaf(fmaf(-sp, sg, sp), kNegInvLog2e, sg);
-      if (r & 1) {
-        const int q = r >> 1;
-        gap[q] = pack_bf16x2(p_ga[r - 1], p_ga[r]);
-        gbp[q] = pack_bf16x2(p_gb[r - 1], p_gb[r]);
-        up[q] = pack_bf16x2(p_u[r - 1], p_u[r]);
+    auto micro = [&](int i) __attribute__((always_inline)) {
+      if (i >= NMICRO) return;
+      const int pr = i / 14, k = i % 14;
+      auto el = [&](int h, auto&& fn2) __attribute__((always_inline)) {
+        const int r = 2 * pr + h, mb = r >> 2, q = r & 3;
+        fn2(h, f.a[mb][q], f.b[mb][q], f.e[mb][q]);
+      };
+      switch (k) {
+        case 0:
+        case 1:
+          el(k, [&](int h, float x, float, float) { g_t[h] = __builtin_amdgcn_exp2f(x); pin(g_t[h]); });
+          break;
+        case 2:
+          el(0, [&](int h, float, float, float) { g_t[h] = 1.f + g_t[h]; pin(g_t[h]); });
+          el(1, [&](int h, float, float, float) { g_t[h] = 1.f + g_t[h]; pin(g_t[h]); });
+          break;
+        case 3:
+        case 4:
+          el(k - 3, [&](int h, float, float, float) { g_sg[h] = __builtin_amdgcn_rcpf(g_t[h]); pin(g_sg[h]); });
+          break;
+        case 5:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float x, float, float) { g_sp[hh] = x * g_sg[hh]; pin(g_sp[hh]); });
+          break;
+        case 6:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float b, float) { g_u[hh] = g_sp[hh] * b; pin(g_u[hh]); });
+          break;
+        case 7:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float, float e) { g_gb[hh] = e * g_sp[hh]; pin(g_gb[hh]); });
+          break;
+        case 8:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float, float) {
+              g_w[hh] = fmaf(-g_sp[hh], g_sg[hh], g_sp[hh]);
+              pin(g_w[hh]);
+            });
+          break;
+        case 9:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float, float) {
+              g_w[hh] = fmaf(g_w[hh], kNegInvLog2e, g_sg[hh]);
+              pin(g_w[hh]);
+            });
+          break;
+        case 10:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float b, float e) { g_eb[hh] = e * b; pin(g_eb[hh]); });
+          break;
+        case 11:
+          for (int h = 0; h < 2; ++h)
+            el(h, [&](int hh, float, float, float) { g_ga[hh] = g_eb[hh] * g_w[hh]; pin(g_ga[hh]); });
+          break;
+        case 12: {
+          unsigned pa = pack_bf16x2(g_ga[0], g_ga[1]), pb = pack_bf16x2(g_gb[0], g_gb[1]);
+          pin(pa);
+          pin(pb);
+          gap[pr] = pa;
+          gbp[pr] = pb;
+          break;
+        }
+        default: {
+          unsigned pu = pack_bf16x2(g_u[0], g_u[1]);
+          pin(pu);
+          up[pr] = pu;
+          break;
+        }
       }
     };
-    Frag2 fr[NSLOT];
-    fr[0] = load_slot(0);
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      if (j + 1 < NSLOT) fr[j + 1] = load_slot(j + 1);
-      if (j < NBS) {
-        bwd_mma(j, fr[j], prev);
-      } else {
-        const int mb = (j - NBS) / KS, ks = (j - NBS) % KS;
-        if (ks == 0) {  // first k-step: start from zero accumulators
-          fn.a[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          fn.b[mb] = fn.a[mb];
-          fn.e[mb] = fn.a[mb];
-        }
-        fwd_mma(fn, mb, ks, fr[j]);
-      }
-      // element rows of the pointwise handled in this slot (16 half-rows
-      // spread over NSLOT slots): even half h = 2r is exp2, odd half the rest
+      if (j + LA < NSLOT) fr[j + LA] = load_slot(t, j + LA);
+      const Frag2& c = fr[j];
 #pragma unroll
-      for (int h = (16 * j) / NSLOT; h < (16 * (j + 1)) / NSLOT; ++h) {
-        const int rr = h >> 1;
-        if ((h & 1) == 0) {
-          p_sg[rr] = __builtin_amdgcn_exp2f(f.a[rr >> 2][rr & 3]);
-          if (rr >= 1) grad_row(rr - 1);
+      for (int q = 0; q < 3; ++q) {
+        if (j < NBS) {
+          if (q == 0) acc1[j] = mfma_bf16(c.x, prev.ga, acc1[j]);
+          if (q == 1) acc3[j] = mfma_bf16(c.x, prev.gb, acc3[j]);
+          if (q == 2) acc2[j] = mfma_bf16(prev.u, c.y, acc2[j]);
         } else {
-          sig_row(rr);
+          const int mb = (j - NBS) / KS, ks = (j - NBS) % KS;
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          if (q == 0) fn.a[mb] = mfma_bf16(c.x, w1f[ks], ks == 0 ? z : fn.a[mb]);
+          if (q == 1) fn.b[mb] = mfma_bf16(c.x, w3f[ks], ks == 0 ? z : fn.b[mb]);
+          if (q == 2) fn.e[mb] = mfma_bf16(c.y, w2f[ks], ks == 0 ? z : fn.e[mb]);
         }
+        micro(3 * j + q);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    grad_row(7);
+#pragma unroll
+    for (int i = 3 * NSLOT; i < NMICRO; ++i) micro(i);
     stage(t + 2);
     __syncthreads();
     cur = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};

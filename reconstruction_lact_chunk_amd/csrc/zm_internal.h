@@ -37,6 +37,14 @@ struct WSet {
   uint16_t* w2tb;  // W2 transposed: [h][d]
 };
 
+// Keeps a computed value in place: an empty volatile asm that takes the value
+// as a register in/out operand, so the compiler must compute it before this
+// point and cannot sink the computation towards its later uses.  Emits no
+// instruction.  Used to interleave independent VALU work with matrix-core
+// work in software-pipelined loops.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+__device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ float bf16lo(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 

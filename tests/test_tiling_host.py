@@ -276,33 +276,35 @@ def _upd_tau(g, j):
     return 16 * (g >> 1) + 4 * (g & 1) + 8 * (j >> 2) + (j & 3)
 
 
-def test_tau_and_swizzle_layout():
-    """Token map and XOR swizzle of the update tile: a bijection; the forward
-    MFMA rows of each lane are the tokens of its backward operand slots; the
-    two transposing reads of a lane share one swizzle; forward row reads,
-    transposing reads and staging writes are free of bank conflicts; and the
+def test_tau_and_tile_layout():
+    """Token map and padded tile of the update kernel: the forward MFMA rows
+    of each lane are the tokens of its backward operand slots; forward row
+    reads, transposing reads and staging writes are free of bank conflicts;
+    every slot's operand address is the lane's base plus a constant; and the
     transposing read delivers tokens tau(g, 0..7) of column 16 m + i."""
     tau = _upd_tau
     for D in (64, 128):
-        def swz(r):
-            return 2 * (r & 7) if D == 128 else 2 * ((r >> 1) & 3)
+        pitch = D + 16  # elements
 
         def off(r, col):  # element offset
-            return r * D + (((col >> 3) ^ swz(r)) << 3) + (col & 7)
+            return r * pitch + col
 
-        assert sorted(off(r, c) for r in range(TOK) for c in range(D)) == list(range(TOK * D))
         assert sorted(tau(g, j) for g in range(4) for j in range(8)) == list(range(TOK))
         for g, c in itertools.product(range(4), range(16)):
             row_a = tau(g, c >> 2)
-            assert row_a + 8 == tau(g, 4 + (c >> 2)) and swz(row_a + 8) == swz(row_a)
+            assert row_a + 8 == tau(g, 4 + (c >> 2))
         for mb, ks in itertools.product(range(2), range(D // 32)):
             addrs = [2 * off(tau((l % 16) >> 2, 4 * mb + (l % 4)), 32 * ks + 8 * (l // 16))
                      for l in range(64)]
             assert read_b128_degree(addrs) == 1
+            base = [2 * off(tau((l % 16) >> 2, l % 4), 8 * (l // 16)) for l in range(64)]
+            assert len({a - b for a, b in zip(addrs, base)}) == 1      # base + constant
         for h, m in itertools.product(range(2), range(D // 16)):
             addrs = [2 * off(tau(l // 16, 4 * h + (l % 16) // 4), 16 * m + 4 * (l % 4))
                      for l in range(64)]
             assert read_b64_degree(addrs) == 1
+            base = [2 * off(tau(l // 16, (l % 16) // 4), 4 * (l % 4)) for l in range(64)]
+            assert len({a - b for a, b in zip(addrs, base)}) == 1
         cpt = D // 8
         for w in range(8):
             items = [64 * w + l for l in range(64) if 64 * w + l < TOK * cpt]
@@ -310,9 +312,8 @@ def test_tau_and_swizzle_layout():
                 addrs = [2 * off(i // cpt, 8 * (i % cpt)) for i in items]
                 assert write_degree(addrs, 16) == 1
         # transposing read: lane i gets element i % 4 of source lanes 4 e + i / 4
-        flat = {off(r, c): (r, c) for r in range(TOK) for c in range(D)}
         for h, m, g in itertools.product(range(2), range(D // 16), range(4)):
-            src = [[flat[off(tau(g, 4 * h + s // 4), 16 * m + 4 * (s % 4)) + x] for x in range(4)]
+            src = [[(tau(g, 4 * h + s // 4), 16 * m + 4 * (s % 4) + x) for x in range(4)]
                    for s in range(16)]
             for i, e in itertools.product(range(16), range(4)):
                 assert src[4 * e + i // 4][i % 4] == (tau(g, 4 * h + e), 16 * m + i)
@@ -322,9 +323,9 @@ def test_tau_and_swizzle_layout():
             assert tau(lane_c >> 2, 4 * mb + (lane_c & 3)) == tau(g, 4 * mb + i)
 
 
-def test_previous_update_swizzle_was_conflicted():
-    # the earlier swizzle 2 (r % 8) + (r / 16) % 2 (D = 128) gives 2-way
-    # conflicts on the forward row reads, as measured (8 cycles, not 4)
+def test_unpadded_swizzled_tile_was_conflicted():
+    # an unpadded tile with swizzle 2 (r % 8) + (r / 16) % 2 (D = 128) gives
+    # 2-way conflicts on the forward row reads, as measured (8 cycles, not 4)
     def off(r, col):
         return r * 128 + (((col >> 3) ^ (2 * (r & 7) + ((r >> 4) & 1))) << 3) + (col & 7)
     addrs = [2 * off(_upd_tau((l % 16) >> 2, l % 4), 8 * (l // 16)) for l in range(64)]
