@@ -156,25 +156,41 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
       for (int nb = 0; nb < NB; ++nb) p1_mma(x, ks, nb, p1_frag(buf, ks, nb));
     return x;
   };
-  // phase-2 slot (tbi, kp): two U^T operands (k-steps 2 kp, 2 kp + 1), 2 MFMAs
+  // Phase-2 slot k: two U^T operands and two MFMAs.  With two token blocks
+  // per wave the slot is k-step k of both blocks (independent accumulators);
+  // with one block it is k-steps 2 k and 2 k + 1 of that block.
   struct Frag2 {
     bf16x8 x, y;
   };
-  auto p2_frag = [&](int buf, int tbi, int kp) {
+  auto p2_frag = [&](int buf, int k) {
     const uint16_t* ub = us[buf & 1];
-    const int r = 16 * (tb0 + tbi) + c;
-    return Frag2{as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * kp))),
-                 as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * kp + 32)))};
+    if constexpr (TBW == 2) {
+      const int r = 16 * tb0 + c;
+      return Frag2{as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 32 * k))),
+                   as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r + 16, 8 * g + 32 * k)))};
+    } else {
+      const int r = 16 * tb0 + c;
+      return Frag2{as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * k))),
+                   as_bf16x8(*(const u32x4*)(ub + u_off<HID>(r, 8 * g + 64 * k + 32)))};
+    }
   };
-  auto p2_mma = [&](f32x4* acc, int tbi, int kp, const Frag2& fr) {
-    if (kp == 0) acc[tbi] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[tbi] = mfma_bf16(w2f[2 * kp], fr.x, acc[tbi]);
-    acc[tbi] = mfma_bf16(w2f[2 * kp + 1], fr.y, acc[tbi]);
+  // q selects the slot's first (0) or second (1) MFMA
+  auto p2_mma1 = [&](f32x4* acc, int k, int q, const Frag2& fr) {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (TBW == 2) {
+      acc[q] = mfma_bf16(w2f[k], q == 0 ? fr.x : fr.y, k == 0 ? z : acc[q]);
+    } else {
+      acc[0] = mfma_bf16(w2f[2 * k + q], q == 0 ? fr.x : fr.y, (k == 0 && q == 0) ? z : acc[0]);
+    }
+  };
+  auto p2_mma = [&](f32x4* acc, int k, const Frag2& fr) {
+    p2_mma1(acc, k, 0, fr);
+    p2_mma1(acc, k, 1, fr);
   };
   // Outputs go through LDS so that each output row leaves as one coalesced
   // 16-byte-per-lane store: phase 2 of tile it writes its results (lane holds
   // O[token 16 tb + c][16 db + 4 g + i]) into os[it % 2], and the next
-  // iteration, after the barrier, stores the tile to memory.
+  // iteration, after the barrier, stores the tile to memory at its end.
   auto o_to_lds = [&](const f32x4* acc, int it) {
 #pragma unroll
     for (int tbi = 0; tbi < TBW; ++tbi) {
@@ -201,8 +217,10 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
     uv[e] = silu_gate(x.a[mb][nb][i], x.b[mb][nb][i]);
   };
-  // U row nb of this wave: hidden j0 + 8 g .. (two row blocks) or j0 + 4 g ..
-  auto write_u = [&](int buf, const float* uv) {
+  // U row nb of this wave: hidden j0 + 8 g .. (two row blocks) or j0 + 4 g ..;
+  // upk[e / 2] holds elements e, e + 1 (element e = (mb * NB + nb) * 4 + i)
+  // packed as bf16.
+  auto write_u = [&](int buf, const unsigned* upk) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       uint16_t* ub = us[buf & 1];
@@ -212,25 +230,33 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
           const int e0 = (mb * NB + nb) * 4;
-          pk[2 * mb] = pack_bf16x2(uv[e0], uv[e0 + 1]);
-          pk[2 * mb + 1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
+          pk[2 * mb] = upk[e0 / 2];
+          pk[2 * mb + 1] = upk[e0 / 2 + 1];
         }
         *(u32x4*)(ub + u_off<HID>(r, j0 + 8 * g)) = pk;
       } else {
         const int e0 = nb * 4;
         u32x2 pk;
-        pk[0] = pack_bf16x2(uv[e0], uv[e0 + 1]);
-        pk[1] = pack_bf16x2(uv[e0 + 2], uv[e0 + 3]);
+        pk[0] = upk[e0 / 2];
+        pk[1] = upk[e0 / 2 + 1];
         *(u32x2*)(ub + u_off<HID>(r, j0 + 4 * g)) = pk;
       }
     }
   };
+  auto gate_all = [&](const Acc1& x, unsigned* upk) {
+    float uv[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) gate_elem(x, e, uv);
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) upk[e / 2] = pack_bf16x2(uv[e], uv[e + 1]);
+  };
 
   // Software pipeline: iteration i gates tile i (VALU), multiplies tile i - 1
   // through W2 (phase 2) and tile i + 1 through W1, W3 (phase 1), as slots of
-  // MFMAs each preceded by the LDS fetch of the next slot and followed by one
-  // element of the gate work; then U(i) goes to LDS, O(i - 1) to memory and
-  // Q(i + 2) is staged.  Two Q and two U buffers; one barrier per iteration.
+  // MFMAs whose LDS operands are fetched two slots ahead; one gate micro-step
+  // follows each MFMA.  Then U(i) goes to LDS, O(i - 1) to LDS, Q(i + 2) is
+  // staged and O(i - 2) leaves for memory.  Two Q, U and O buffers; one
+  // barrier per iteration; wave priority follows progress through the slots.
   constexpr int NS2 = TBW * KS2 / 2;   // phase-2 slots
   constexpr int NS1 = KS1 * NB;        // phase-1 slots
   constexpr int NSLOT = NS1 + NS2;
@@ -243,11 +269,10 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
   __syncthreads();  // every wave is done with Q(0) before Q(2) reuses its buffer
   f32x4 acc2[TBW];
   {  // i = 0: no phase 2 yet
-    float uv[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) gate_elem(cur, e, uv);
+    unsigned upk[NE / 2];
+    gate_all(cur, upk);
     if (ntiles > 1) cur = phase1(1);
-    write_u(0, uv);
+    write_u(0, upk);
     fetch(2);
     stage(2);
     __syncthreads();
@@ -264,48 +289,107 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     constexpr int both = 2 * (NS1 < NS2 ? NS1 : NS2);
     return j < both ? (j >> 1) : (j - both / 2);
   };
-  auto step = [&](int it, const Acc1& cur, Acc1& nxt) {
+  // Gate micro-steps: elements in groups of four chains, 15 micro-steps per
+  // group (four exp2, two steps of two adds, four reciprocals, two steps of
+  // two products with x, two with b, one pair of bf16 packs), each at most
+  // two plain VALU operations or one transcendental, so that one fits in the
+  // shadow of one MFMA.
+  constexpr int NMICRO = (NE / 4) * 15;
+  auto step = [&](int it, const Acc1& cur, Acc1& nxt) __attribute__((always_inline)) {
     fetch(it + 2);
-    if (it >= 2) o_from_lds(it - 2);
-    float ev[NE], sv[NE], uv[NE];
     Frag2 f2[NSLOT];
     bf16x8 f1[NSLOT];
     auto load_slot = [&](int j) {
       const int k = slot_idx(j);
-      if (slot_is_p2(j)) f2[j] = p2_frag(it - 1, k / (KS2 / 2), k % (KS2 / 2));
+      if (slot_is_p2(j)) f2[j] = p2_frag(it - 1, k);
       else f1[j] = p1_frag(it + 1, k / NB, k % NB);
     };
-    auto gate_a = [&](int e) {
-      const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
-      ev[e] = __builtin_amdgcn_exp2f(cur.a[mb][nb][i]);
+    float gt[4], gy[4];
+    unsigned upk[NE / 2];
+    auto micro = [&](int m) __attribute__((always_inline)) {
+      if (m >= NMICRO) return;
+      const int grp = m / 15, k = m % 15;
+      auto xv = [&](int h) {
+        const int e = 4 * grp + h, i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
+        return cur.a[mb][nb][i];
+      };
+      auto bv = [&](int h) {
+        const int e = 4 * grp + h, i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
+        return cur.b[mb][nb][i];
+      };
+      if (k < 4) {
+        gt[k] = __builtin_amdgcn_exp2f(xv(k));
+        pin(gt[k]);
+      } else if (k < 6) {
+        const int h = 2 * (k - 4);
+        gt[h] = 1.f + gt[h];
+        gt[h + 1] = 1.f + gt[h + 1];
+        pin(gt[h]);
+        pin(gt[h + 1]);
+      } else if (k < 10) {
+        gt[k - 6] = __builtin_amdgcn_rcpf(gt[k - 6]);
+        pin(gt[k - 6]);
+      } else if (k < 12) {
+        const int h = 2 * (k - 10);
+        gy[h] = xv(h) * gt[h];
+        gy[h + 1] = xv(h + 1) * gt[h + 1];
+        pin(gy[h]);
+        pin(gy[h + 1]);
+      } else if (k < 14) {
+        const int h = 2 * (k - 12);
+        gy[h] = gy[h] * bv(h);
+        gy[h + 1] = gy[h + 1] * bv(h + 1);
+        pin(gy[h]);
+        pin(gy[h + 1]);
+      } else {
+        unsigned p0 = pack_bf16x2(gy[0], gy[1]), p1 = pack_bf16x2(gy[2], gy[3]);
+        pin(p0);
+        pin(p1);
+        upk[2 * grp] = p0;
+        upk[2 * grp + 1] = p1;
+      }
     };
-    auto gate_b = [&](int e) { sv[e] = __builtin_amdgcn_rcpf(1.f + ev[e]); };
-    auto gate_c = [&](int e) {
-      const int i = e & 3, nb = (e >> 2) % NB, mb = (e >> 2) / NB;
-      uv[e] = cur.a[mb][nb][i] * sv[e] * cur.b[mb][nb][i];
-    };
-    load_slot(0);
+    constexpr int LA = 2;  // LDS operand lookahead, in slots
+#pragma unroll
+    for (int j = 0; j < LA; ++j) load_slot(j);
+    int mi = 0;
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      if (j + 1 < NSLOT) load_slot(j + 1);
+      set_progress_priority<NSLOT>(j);
+      if (j + LA < NSLOT) load_slot(j + LA);
       const int k = slot_idx(j);
-      if (slot_is_p2(j)) p2_mma(acc2, k / (KS2 / 2), k % (KS2 / 2), f2[j]);
-      else p1_mma(nxt, k / NB, k % NB, f1[j]);
-      const int lo = (NE * j) / NSLOT, hi = (NE * (j + 1)) / NSLOT;
+      if (slot_is_p2(j)) {
+        p2_mma1(acc2, k, 0, f2[j]);
+        micro(mi++);
+        __builtin_amdgcn_sched_barrier(0);
+        p2_mma1(acc2, k, 1, f2[j]);
+        micro(mi++);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        const int ks = k / NB, nb = k % NB;
 #pragma unroll
-      for (int e = lo; e < hi; ++e) {
-        gate_a(e);
-        if (e >= 1) gate_b(e - 1);
-        if (e >= 2) gate_c(e - 2);
+        for (int mb = 0; mb < MB1; ++mb) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          nxt.a[mb][nb] = mfma_bf16(w1f[mb][ks], f1[j], ks == 0 ? z : nxt.a[mb][nb]);
+          micro(mi++);
+          __builtin_amdgcn_sched_barrier(0);
+          nxt.b[mb][nb] = mfma_bf16(w3f[mb][ks], f1[j], ks == 0 ? z : nxt.b[mb][nb]);
+          micro(mi++);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    gate_b(NE - 1);
-    gate_c(NE - 2);
-    gate_c(NE - 1);
-    write_u(it, uv);
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int m = 0; m < NMICRO; ++m)
+      if (m >= mi) micro(m);
+    write_u(it, upk);
     o_to_lds(acc2, it - 1);
     stage(it + 2);
+    // Output tile it - 2 (in LDS since the previous iteration) leaves last,
+    // so that its store has a whole iteration to complete before the next
+    // wait on the memory counter.
+    if (it >= 2) o_from_lds(it - 2);
     __syncthreads();
   };
   Acc1 alt;
@@ -320,22 +404,17 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
   }
   if (ntiles > 1) {  // i = ntiles - 1: no phase 1
     if (ntiles >= 3) o_from_lds(ntiles - 3);
-    float uv[NE];
+    unsigned upk[NE / 2];
+    gate_all(cur, upk);
 #pragma unroll
-    for (int e = 0; e < NE; ++e) gate_elem(cur, e, uv);
-#pragma unroll
-    for (int tbi = 0; tbi < TBW; ++tbi)
-#pragma unroll
-      for (int kp = 0; kp < KS2 / 2; ++kp) p2_mma(acc2, tbi, kp, p2_frag(ntiles - 2, tbi, kp));
-    write_u(ntiles - 1, uv);
+    for (int k = 0; k < NS2; ++k) p2_mma(acc2, k, p2_frag(ntiles - 2, k));
+    write_u(ntiles - 1, upk);
     o_to_lds(acc2, ntiles - 2);
     __syncthreads();
     o_from_lds(ntiles - 2);
   }
 #pragma unroll
-  for (int tbi = 0; tbi < TBW; ++tbi)
-#pragma unroll
-    for (int kp = 0; kp < KS2 / 2; ++kp) p2_mma(acc2, tbi, kp, p2_frag(ntiles - 1, tbi, kp));
+  for (int k = 0; k < NS2; ++k) p2_mma(acc2, k, p2_frag(ntiles - 1, k));
   o_to_lds(acc2, ntiles - 1);
   __syncthreads();
   o_from_lds(ntiles - 1);

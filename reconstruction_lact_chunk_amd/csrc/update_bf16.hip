@@ -387,6 +387,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     };
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
+      set_progress_priority<NSLOT>(j);
       if (j + LA < NSLOT) fr[j + LA] = load_slot(t, j + LA);
       const Frag2& c = fr[j];
 #pragma unroll
@@ -406,6 +407,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 3 * NSLOT; i < NMICRO; ++i) micro(i);
     stage(t + 2);

@@ -42,6 +42,19 @@ struct WSet {
 // point and cannot sink the computation towards its later uses.  Emits no
 // instruction.  Used to interleave independent VALU work with matrix-core
 // work in software-pipelined loops.
+// Wave priority from progress through the N slots of a pipelined iteration:
+// 3 in the first quarter down to 0 in the last.  Two waves share a SIMD and
+// the older one otherwise always wins issue, finishing early and idling at
+// the barrier while the other runs alone; with priority falling as a wave
+// advances, the wave that is behind is preferred and both arrive together.
+template <int N>
+__device__ __forceinline__ void set_progress_priority(int slot) {
+  if (slot == 0) __builtin_amdgcn_s_setprio(3);
+  if (slot == N / 4) __builtin_amdgcn_s_setprio(2);
+  if (slot == N / 2) __builtin_amdgcn_s_setprio(1);
+  if (slot == (3 * N) / 4) __builtin_amdgcn_s_setprio(0);
+}
+
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ void pin(unsigned& x) { asm volatile("" : "+v"(x)); }
 

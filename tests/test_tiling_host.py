@@ -366,9 +366,12 @@ def test_apply_tiles_conflict_free(D, H):
             assert write_degree(addrs, 8) == 2
     for w in range(8):                                             # phase-2 U reads
         tb0 = (w // db_n) * tbw
-        for tbi, kp, y in itertools.product(range(tbw), range(H // 64), range(2)):
-            addrs = [2 * u_off(16 * (tb0 + tbi) + l % 16, 8 * (l // 16) + 64 * kp + 32 * y)
-                     for l in range(64)]
+        if tbw == 2:   # slot k: k-step k of both token blocks
+            reads = [(16 * (tb0 + y), 32 * k) for k in range(H // 32) for y in range(2)]
+        else:          # slot k: k-steps 2 k and 2 k + 1 of the one block
+            reads = [(16 * tb0, 64 * k + 32 * y) for k in range(H // 64) for y in range(2)]
+        for row0, col0 in reads:
+            addrs = [2 * u_off(row0 + l % 16, col0 + 8 * (l // 16)) for l in range(64)]
             assert read_b128_degree(addrs) == 1
     for w in range(8):                                             # O writes (8 bytes)
         db, tb0 = w % db_n, (w // db_n) * tbw
