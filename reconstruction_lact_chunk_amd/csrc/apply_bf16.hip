@@ -355,7 +355,7 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     int mi = 0;
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      set_progress_priority<NSLOT>(j);
+      set_progress_priority<NSLOT, false>(j);
       if (j + LA < NSLOT) load_slot(j + LA);
       const int k = slot_idx(j);
       if (slot_is_p2(j)) {

@@ -44,6 +44,7 @@ struct UpdCfg {
   static constexpr int ITEMS = T * CPT;         // staging items per tile
   static constexpr int TILE = T * (D + 16);      // elements per padded tile
   static constexpr int BUF = 2 * TILE;           // elements per LDS buffer (K tile, V_eta tile)
+  static constexpr int NBUF = 8;                 // LDS buffers (tile t in buffer t % NBUF)
   static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
 };
 
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk) {
   using C = UpdCfg<D, HID>;
   constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * C::BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[C::NBUF * C::BUF];
 
   // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
   // over the 8 XCDs; the slices of one (head, chunk) get ids 8 apart, so they
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     if constexpr (C::ITEMS < kWaves * 64) {
       if (!has_item) return;
     }
-    uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     uint16_t* vtm = ktm + C::TILE;
     u32x4 vs;
 #pragma unroll
@@ -196,7 +197,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
 
   // forward A = K W1^T, B = K W3^T, E = V_eta W2 on one tile (24 MFMAs)
   auto forward = [&](int buf) {
-    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     const uint16_t* vtm = ktm + C::TILE;
     Fwd f;
 #pragma unroll
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
 
   // backward D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta (24 MFMAs)
   auto backward = [&](int buf, const Grad& gr) {
-    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     const uint16_t* vtm = ktm + C::TILE;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     bf16x8 x, y;
   };
   auto fwd_frag = [&](int buf, int mb, int ks) {  // K and V_eta rows (A operands)
-    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     const int off = tile_off<D>(tau(c >> 2, 4 * mb + (c & 3)), 32 * ks + 8 * g);
     return Frag2{as_bf16x8(*(const u32x4*)(ktm + off)),
                  as_bf16x8(*(const u32x4*)(ktm + C::TILE + off))};
@@ -274,7 +275,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     f.e[mb] = mfma_bf16(fr.y, w2f[ks], f.e[mb]);
   };
   auto bwd_frag = [&](int buf, int m) {  // K^T and V_eta^T column pieces
-    const uint16_t* ktm = lds + (buf & 3) * C::BUF;
+    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     const int col = 16 * m + 4 * (c & 3);
     const int oa = tile_off<D>(row_a, col), ob = tile_off<D>(row_b, col);
     return Frag2{__builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
@@ -307,9 +308,9 @@ __global__ __launch_bounds__(512) void k_update_bf16(
   // keeps this placement.  The loop is unrolled by two so the carried state
   // alternates between two register sets instead of being copied.
   constexpr int NMICRO = 4 * 14;
-  auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur)
+  auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur, bool barrier)
       __attribute__((always_inline)) {
-    fetch(t + 2);
+    fetch(t + 3);
     Frag2 fr[NSLOT];
 #pragma unroll
     for (int j = 0; j < LA; ++j) fr[j] = load_slot(t, j);
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     };
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      set_progress_priority<NSLOT>(j);
+      set_progress_priority<NSLOT, true>(j);
       if (j + LA < NSLOT) fr[j + LA] = load_slot(t, j + LA);
       const Frag2& c = fr[j];
 #pragma unroll
@@ -410,31 +411,38 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 3 * NSLOT; i < NMICRO; ++i) micro(i);
-    stage(t + 2);
-    __syncthreads();
+    stage(t + 3);
+    if (barrier) __syncthreads();
     cur = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
   };
 
+  // Tile t is staged in iteration t - 3 (the prologue stages tiles 0..3),
+  // read by the forward in iteration t - 1 and by the backward in iteration
+  // t + 1.  A barrier closes every even iteration only: a staged tile is
+  // first read two iterations later, and a buffer is rewritten (NBUF = 8)
+  // four iterations after its last read, so a barrier always lies between.
   if (ntiles > 0) {
     fetch(0);
     stage(0);
     fetch(1);
     stage(1);
+    fetch(2);
+    stage(2);
     __syncthreads();
     Fwd fa = forward(0), fb;
     Grad ga_ = pointwise(fa), gb_;
     // t = 0: no backward yet
-    fetch(2);
+    fetch(3);
     if (ntiles > 1) fa = forward(1);
-    stage(2);
+    stage(3);
     __syncthreads();
     int t = 1;
     for (; t + 2 < ntiles; t += 2) {  // steady state, two iterations per trip
-      step(t, fa, ga_, fb, gb_);
-      step(t + 1, fb, gb_, fa, ga_);
+      step(t, fa, ga_, fb, gb_, false);
+      step(t + 1, fb, gb_, fa, ga_, true);
     }
     if (t + 1 < ntiles) {  // one steady iteration left
-      step(t, fa, ga_, fb, gb_);
+      step(t, fa, ga_, fb, gb_, true);
       fa = fb;
       ga_ = gb_;
       ++t;

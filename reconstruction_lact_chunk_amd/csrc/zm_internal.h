@@ -47,12 +47,25 @@ struct WSet {
 // the older one otherwise always wins issue, finishing early and idling at
 // the barrier while the other runs alone; with priority falling as a wave
 // advances, the wave that is behind is preferred and both arrive together.
-template <int N>
+// With YOUNG_BIAS the younger wave of each pair (waves 4..7 of 8) stays one
+// level higher after the first quarter (3, 3, 2, 1), which balances the
+// update kernel better; the apply kernel runs best without it.
+template <int N, bool YOUNG_BIAS>
 __device__ __forceinline__ void set_progress_priority(int slot) {
+  const bool young = YOUNG_BIAS && (threadIdx.x >> 6) >= 4;
   if (slot == 0) __builtin_amdgcn_s_setprio(3);
-  if (slot == N / 4) __builtin_amdgcn_s_setprio(2);
-  if (slot == N / 2) __builtin_amdgcn_s_setprio(1);
-  if (slot == (3 * N) / 4) __builtin_amdgcn_s_setprio(0);
+  if (slot == N / 4) {
+    if (young) __builtin_amdgcn_s_setprio(3);
+    else __builtin_amdgcn_s_setprio(2);
+  }
+  if (slot == N / 2) {
+    if (young) __builtin_amdgcn_s_setprio(2);
+    else __builtin_amdgcn_s_setprio(1);
+  }
+  if (slot == (3 * N) / 4) {
+    if (young) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+  }
 }
 
 __device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }

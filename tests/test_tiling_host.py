@@ -83,8 +83,9 @@ def test_update_chunks_partition_and_loads_in_bounds(n, heads, d_hidden):
         assert tb < te, "no empty chunk"
         covered.append((tb, te))
         ntiles = ceil_div(te - tb, TOK)
-        # the pipeline fetches tiles 0 .. ntiles + 1 (two past the end at most)
-        for it in range(ntiles + 2):
+        # the pipeline fetches tiles 0 .. max(3, ntiles + 1): the prologue
+        # fetches tiles 0..3, iteration t fetches tile t + 3
+        for it in range(max(4, ntiles + 2)):
             for r in fetch_rows_update(tb, te, it):
                 assert tb <= r < te <= n
     assert covered[0][0] == 0 and covered[-1][1] == n
@@ -108,12 +109,12 @@ def test_apply_chunks_partition_and_loads_in_bounds(n, heads):
 
 
 def check_schedule(intervals, nbuf):
-    """intervals: list of dicts with 'read' and 'write' lists of tile ids.
-    A tile t lives in buffer t % nbuf.  Checks: no buffer is read and written
-    in one interval; a tile is written before it is read in a later interval;
-    a buffer is not overwritten while a tile in it is still to be read."""
+    """intervals: list of dicts with 'read' and 'write' lists of tile ids,
+    one per stretch between barriers.  A tile t lives in buffer t % nbuf.
+    Checks: no buffer is read and written in one interval; a tile is written
+    in an earlier interval than any read of it; a buffer is not overwritten
+    while a tile in it is still to be read."""
     written = {}
-    last_read_needed = {}
     for k, iv in enumerate(intervals):
         rb = {t % nbuf for t in iv["read"]}
         wb = {t % nbuf for t in iv["write"]}
@@ -130,14 +131,23 @@ def check_schedule(intervals, nbuf):
 
 
 def update_schedule(ntiles):
-    ivs = [{"read": [], "write": [0, 1]}]                       # prologue staging
-    ivs.append({"read": [0, 1], "write": [2]})                   # forward(0); t = 0
+    """Barrier intervals of the update kernel: tiles 0..2 staged, barrier;
+    forward(0), forward(1) and staging of tile 3, barrier; then iteration t
+    reads tiles t - 1 (backward) and t + 1 (forward) and stages tile t + 3,
+    with a barrier after every even iteration (and after the last steady
+    iteration); the epilogue reads the last two tiles."""
+    ivs = [{"read": [], "write": [0, 1, 2]},
+           {"read": [0, 1], "write": [3]}]
+    cur = {"read": [], "write": []}
+    last = ntiles - 2                       # last steady iteration
     for t in range(1, ntiles - 1):
-        ivs.append({"read": [t - 1, t + 1], "write": [t + 2]})   # backward, forward, stage
-    if ntiles > 1:
-        ivs.append({"read": [ntiles - 2, ntiles - 1], "write": []})
-    else:
-        ivs.append({"read": [0], "write": []})
+        cur["read"] += [t - 1, t + 1]
+        cur["write"] += [t + 3]
+        if t % 2 == 0 or t == last:
+            ivs.append(cur)
+            cur = {"read": [], "write": []}
+    assert not cur["read"]
+    ivs.append({"read": [ntiles - 2, ntiles - 1] if ntiles > 1 else [0], "write": []})
     return ivs
 
 
@@ -175,10 +185,10 @@ def apply_o_schedule(ntiles):
     return ivs
 
 
-@pytest.mark.parametrize("ntiles", list(range(1, 12)))
+@pytest.mark.parametrize("ntiles", list(range(1, 14)))
 def test_pipeline_buffer_schedules_are_hazard_free(ntiles):
     # tiles past the last are staged (prefetch overrun) but never read
-    check_schedule(update_schedule(ntiles), 4)
+    check_schedule(update_schedule(ntiles), 8)
     check_schedule(apply_q_schedule(ntiles), 2)
     check_schedule(apply_u_schedule(ntiles), 2)
     sched = apply_o_schedule(ntiles)
@@ -186,6 +196,16 @@ def test_pipeline_buffer_schedules_are_hazard_free(ntiles):
     # every output tile is written once and stored once
     assert sorted(t for iv in sched for t in iv["write"]) == list(range(ntiles))
     assert sorted(t for iv in sched for t in iv["read"]) == list(range(ntiles))
+
+
+def test_update_schedule_needs_eight_buffers_or_six():
+    # six buffers are the fewest that keep the every-other-iteration barrier
+    # scheme hazard free; five let staging overwrite a tile still to be read
+    for ntiles in range(6, 14):
+        check_schedule(update_schedule(ntiles), 6)
+    with pytest.raises(AssertionError):
+        for ntiles in range(6, 14):
+            check_schedule(update_schedule(ntiles), 5)
 
 
 def test_schedule_checker_catches_a_missing_barrier():
