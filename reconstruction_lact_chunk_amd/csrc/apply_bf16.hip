@@ -201,16 +201,21 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     }
   };
   const int o_lane_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : 0;
-  auto o_from_lds = [&](int it) {
+  // Reading an output tile back from LDS and storing it are separate steps,
+  // so the read can be issued early in an iteration and the store late.
+  auto o_read = [&](int it) {
+    const uint16_t* src = &os[it & 1][(has_item ? s_tok : 0) * C::OP + 8 * s_ch];
+    const u32x2 lo = *(const u32x2*)(src), hi = *(const u32x2*)(src + 4);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto o_store = [&](int it, const u32x4& v) {
     if constexpr (C::ITEMS < kWaves * 64) {
       if (!has_item) return;
     }
     const int64_t tile0 = t_begin + (int64_t)it * T;
-    const uint16_t* src = &os[it & 1][s_tok * C::OP + 8 * s_ch];
-    const u32x2 lo = *(const u32x2*)(src), hi = *(const u32x2*)(src + 4);
-    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
     if (tile0 + s_tok < t_end) *(u32x4*)(op + tile0 * ld + o_lane_off) = v;
   };
+  auto o_from_lds = [&](int it) { o_store(it, o_read(it)); };
   // SiLU gate of element e (= (mb * NB + nb) * 4 + i) into the packed U rows
   constexpr int NE = MB1 * NB * 4;
   auto gate_elem = [&](const Acc1& x, int e, float* uv) {
@@ -353,9 +358,11 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
 #pragma unroll
     for (int j = 0; j < LA; ++j) load_slot(j);
     int mi = 0;
+    u32x4 ov = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
       set_progress_priority<NSLOT, false>(j);
+      if (j == 2 && it >= 2) ov = o_read(it - 2);  // output tile it - 2, stored at the end
       if (j + LA < NSLOT) load_slot(j + LA);
       const int k = slot_idx(j);
       if (slot_is_p2(j)) {
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     // Output tile it - 2 (in LDS since the previous iteration) leaves last,
     // so that its store has a whole iteration to complete before the next
     // wait on the memory counter.
-    if (it >= 2) o_from_lds(it - 2);
+    if (it >= 2) o_store(it - 2, ov);
     __syncthreads();
   };
   Acc1 alt;
