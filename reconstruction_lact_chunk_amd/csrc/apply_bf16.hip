@@ -361,7 +361,7 @@ __global__ __launch_bounds__(512) void k_apply_bf16(
     u32x4 ov = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      set_progress_priority<NSLOT, false>(j);
+      set_progress_priority<NSLOT, 3, 1, 0>(j);
       if (j == 2 && it >= 2) ov = o_read(it - 2);  // output tile it - 2, stored at the end
       if (j + LA < NSLOT) load_slot(j + LA);
       const int k = slot_idx(j);

@@ -388,7 +388,7 @@ __global__ __launch_bounds__(512) void k_update_bf16(
     };
 #pragma unroll
     for (int j = 0; j < NSLOT; ++j) {
-      set_progress_priority<NSLOT, true>(j);
+      set_progress_priority<NSLOT, 3, 2, 1>(j);
       if (j + LA < NSLOT) fr[j + LA] = load_slot(t, j + LA);
       const Frag2& c = fr[j];
 #pragma unroll

@@ -36,87 +36,84 @@ hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int he
   return hipGetLastError();
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-  // Butterfly: every lane ends with the same bits (each step adds the same
-  // pair of operands on both partner lanes).
+// Sum over the TPR lanes of an aligned lane group (TPR a power of two <= 64)
+// by butterfly: every lane of the group ends with the same bits, since each
+// step adds the same two operands on both partner lanes.
+template <int TPR>
+__device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
+  for (int m = TPR / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
 
-// One wave per weight row.  Rows of a head: h rows of W1 (length d), h rows
-// of W3 (length d), d rows of W2 (length h).  part: [S][H][3][h*d] with the
-// three matrices in their natural layouts ([h][d], [h][d], [d][h]).
-template <int MAXE>
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int splits,
-                                                int heads, int d, int h,
-                                                const float* w1, const float* w2,
-                                                const float* w3, float* o1, float* o2,
-                                                float* o3, int renorm, WSet ob, int emit_bf16) {
-  const int rows_per_head = 2 * h + d;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (wave >= heads * rows_per_head) return;
-  const int head = wave / rows_per_head;
-  const int r = wave - head * rows_per_head;
-  int mat, row, len;
-  if (r < h) {
-    mat = 0; row = r; len = d;
-  } else if (r < 2 * h) {
-    mat = 1; row = r - h; len = d;
-  } else {
-    mat = 2; row = r - 2 * h; len = h;
-  }
-  const float* win = mat == 0 ? w1 : (mat == 1 ? w3 : w2);
-  float* wout = mat == 0 ? o1 : (mat == 1 ? o3 : o2);
-  const int64_t hd_elems = (int64_t)h * d;
-  const int64_t base = (int64_t)head * hd_elems + (int64_t)row * len;
-  const float* pbase = part + ((int64_t)head * 3 + mat) * hd_elems + (int64_t)row * len;
-  const int64_t pstride = (int64_t)heads * 3 * hd_elems;
-  const int ne = len / 64;
-
-  float wv[MAXE], nv[MAXE];
-#pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    wv[e] = 0.f;
-    nv[e] = 0.f;
-    if (e < ne) {
-      const int col = lane + 64 * e;
-      float s = 0.f;
-      for (int si = 0; si < splits; ++si) s += pbase[si * pstride + col];  // fixed order
-      wv[e] = win[base + col];
-      nv[e] = wv[e] + s;
-    }
-  }
+// One thread per 4 consecutive elements of the [H][3][h*d] weight space (the
+// partials' layout): rows of W1, W3 (length d) and W2 (length h) are
+// contiguous, so the LEN / 4 threads of a row form an aligned lane group of
+// one wave.  Each thread adds the S partials of its 4 elements in split order
+// (fixed order: bitwise reproducible), forms W' = W + sum, and for renorm
+// scales its row by ||W_row|| / max(||W'_row||, 1e-12) with both norms summed
+// over the row's lane group.  16-byte loads keep all S partial reads in flight.
+template <int LEN>
+__device__ __forceinline__ void reduce_row4(const float* __restrict__ part, int splits,
+                                            int64_t pstride, int64_t e, const float* win,
+                                            float* wout, int renorm, f32x4& nv) {
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int si = 0; si < splits; ++si) sum += *(const f32x4*)(part + si * pstride + e);
+  const f32x4 wv = *(const f32x4*)(win);
+  nv = wv + sum;
   if (renorm) {
     float so = 0.f, sn = 0.f;
 #pragma unroll
-    for (int e = 0; e < MAXE; ++e) {
-      so = fmaf(wv[e], wv[e], so);
-      sn = fmaf(nv[e], nv[e], sn);
+    for (int q = 0; q < 4; ++q) {
+      so = fmaf(wv[q], wv[q], so);
+      sn = fmaf(nv[q], nv[q], sn);
     }
-    so = wave_sum(so);
-    sn = wave_sum(sn);
+    so = group_sum<LEN / 4>(so);
+    sn = group_sum<LEN / 4>(sn);
     // Same code on identical values: an unchanged row gets scale exactly 1.
     const float scale = sqrtf(so) / fmaxf(sqrtf(sn), 1e-12f);
-#pragma unroll
-    for (int e = 0; e < MAXE; ++e) nv[e] *= scale;
+    nv *= scale;
   }
+  *(f32x4*)(wout) = nv;
+}
+
+template <int D, int HID>
+__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int splits,
+                                                int heads, const float* w1, const float* w2,
+                                                const float* w3, float* o1, float* o2, float* o3,
+                                                int renorm, WSet ob, int emit_bf16) {
+  constexpr int64_t HD = (int64_t)HID * D;
+  const int64_t e = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);  // element index
+  if (e >= (int64_t)heads * 3 * HD) return;
+  const int64_t head = e / (3 * HD);
+  const int64_t rem = e - head * 3 * HD;
+  const int mat = (int)(rem / HD);
+  const int64_t local = rem - mat * HD;
+  const int64_t off = head * HD + local;  // offset in the weight and bf16 arrays
+  const int64_t pstride = (int64_t)heads * 3 * HD;
+  f32x4 nv;
+  if (mat == 2) {  // W2 rows have length h
+    reduce_row4<HID>(part, splits, pstride, e, w2 + off, o2 + off, renorm, nv);
+  } else {         // W1 / W3 rows have length d
+    reduce_row4<D>(part, splits, pstride, e, (mat == 0 ? w1 : w3) + off, (mat == 0 ? o1 : o3) + off,
+                   renorm, nv);
+  }
+  if (emit_bf16) {
+    if (mat == 0) {
+      u32x2 pk = {pack_bf16x2(kNegLog2e * nv[0], kNegLog2e * nv[1]),
+                  pack_bf16x2(kNegLog2e * nv[2], kNegLog2e * nv[3])};
+      *(u32x2*)(ob.w1b + off) = pk;
+    } else if (mat == 1) {
+      u32x2 pk = {pack_bf16x2(nv[0], nv[1]), pack_bf16x2(nv[2], nv[3])};
+      *(u32x2*)(ob.w3b + off) = pk;
+    } else {
+      u32x2 pk = {pack_bf16x2(kNegInvLog2e * nv[0], kNegInvLog2e * nv[1]),
+                  pack_bf16x2(kNegInvLog2e * nv[2], kNegInvLog2e * nv[3])};
+      *(u32x2*)(ob.w2b + off) = pk;
+      // transposed copy: w2tb[head][j][c] = W2[head][c][j]
+      const int64_t c = local / HID, j = local - c * HID;
 #pragma unroll
-  for (int e = 0; e < MAXE; ++e) {
-    if (e < ne) {
-      const int col = lane + 64 * e;
-      wout[base + col] = nv[e];
-      if (emit_bf16) {
-        if (mat == 0) {
-          ob.w1b[base + col] = to_bf16(kNegLog2e * nv[e]);
-        } else if (mat == 1) {
-          ob.w3b[base + col] = to_bf16(nv[e]);
-        } else {
-          ob.w2b[base + col] = to_bf16(kNegInvLog2e * nv[e]);
-          ob.w2tb[((int64_t)head * h + col) * d + row] = to_bf16(nv[e]);
-        }
-      }
+      for (int q = 0; q < 4; ++q) ob.w2tb[(head * HID + j + q) * D + c] = to_bf16(nv[q]);
     }
   }
 }
@@ -125,18 +122,19 @@ hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
                          const float* w1, const float* w2, const float* w3, float* o1,
                          float* o2, float* o3, int renorm, const WSet* out_bf16,
                          hipStream_t st) {
-  const int rows = heads * (2 * h + d);
-  const unsigned blocks = (unsigned)ceil_div(rows, 4);
+  const int64_t threads = (int64_t)heads * 3 * h * d / 4;
+  const unsigned blocks = (unsigned)ceil_div(threads, 256);
   WSet ob = out_bf16 ? *out_bf16 : WSet{nullptr, nullptr, nullptr, nullptr};
   const int emit = out_bf16 ? 1 : 0;
-  const int maxlen = h > d ? h : d;
-  if (maxlen <= 128) {
-    hipLaunchKernelGGL(k_reduce<2>, dim3(blocks), dim3(256), 0, st, part, splits, heads, d, h,
-                       w1, w2, w3, o1, o2, o3, renorm, ob, emit);
-  } else {
-    hipLaunchKernelGGL(k_reduce<4>, dim3(blocks), dim3(256), 0, st, part, splits, heads, d, h,
-                       w1, w2, w3, o1, o2, o3, renorm, ob, emit);
-  }
+#define ZM_LAUNCH_RED(DD, HH)                                                                   \
+  hipLaunchKernelGGL((k_reduce<DD, HH>), dim3(blocks), dim3(256), 0, st, part, splits, heads, w1, \
+                     w2, w3, o1, o2, o3, renorm, ob, emit)
+  if (d == 128 && h == 256) ZM_LAUNCH_RED(128, 256);
+  else if (d == 128 && h == 128) ZM_LAUNCH_RED(128, 128);
+  else if (d == 64 && h == 256) ZM_LAUNCH_RED(64, 256);
+  else if (d == 64 && h == 128) ZM_LAUNCH_RED(64, 128);
+  else return hipErrorInvalidValue;
+#undef ZM_LAUNCH_RED
   return hipGetLastError();
 }
 

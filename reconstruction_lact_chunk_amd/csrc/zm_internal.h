@@ -42,28 +42,27 @@ struct WSet {
 // point and cannot sink the computation towards its later uses.  Emits no
 // instruction.  Used to interleave independent VALU work with matrix-core
 // work in software-pipelined loops.
-// Wave priority from progress through the N slots of a pipelined iteration:
-// 3 in the first quarter down to 0 in the last.  Two waves share a SIMD and
-// the older one otherwise always wins issue, finishing early and idling at
-// the barrier while the other runs alone; with priority falling as a wave
-// advances, the wave that is behind is preferred and both arrive together.
-// With YOUNG_BIAS the younger wave of each pair (waves 4..7 of 8) stays one
-// level higher after the first quarter (3, 3, 2, 1), which balances the
-// update kernel better; the apply kernel runs best without it.
-template <int N, bool YOUNG_BIAS>
+// Wave priority from progress through the N slots of a pipelined iteration,
+// changed at each quarter.  Two waves share a SIMD and the older one
+// otherwise always wins issue, finishing early and idling at the barrier
+// while the other runs alone; with priority falling as a wave advances, the
+// wave that is behind is preferred and both arrive together.  The older wave
+// of each pair (waves 0..3 of 8) steps 3, 2, 1, 0; the younger one (waves
+// 4..7) steps 3, Y1, Y2, Y3, tuned per kernel.
+template <int N, int Y1, int Y2, int Y3>
 __device__ __forceinline__ void set_progress_priority(int slot) {
-  const bool young = YOUNG_BIAS && (threadIdx.x >> 6) >= 4;
+  const bool young = (threadIdx.x >> 6) >= 4;
   if (slot == 0) __builtin_amdgcn_s_setprio(3);
   if (slot == N / 4) {
-    if (young) __builtin_amdgcn_s_setprio(3);
+    if (young) __builtin_amdgcn_s_setprio(Y1);
     else __builtin_amdgcn_s_setprio(2);
   }
   if (slot == N / 2) {
-    if (young) __builtin_amdgcn_s_setprio(2);
+    if (young) __builtin_amdgcn_s_setprio(Y2);
     else __builtin_amdgcn_s_setprio(1);
   }
   if (slot == (3 * N) / 4) {
-    if (young) __builtin_amdgcn_s_setprio(1);
+    if (young) __builtin_amdgcn_s_setprio(Y3);
     else __builtin_amdgcn_s_setprio(0);
   }
 }
