@@ -19,12 +19,16 @@ from .ttt_oracle import (  # noqa: F401
     chunk_gradient,
     gradient_step,
     renorm_rows,
+    newton_schulz,
+    MUON_NS_COEFFS,
+    NS_STEPS,
     update_head,
     apply_head,
     update,
     apply,
     update_apply,
     stream,
+    chunked,
     virtual_loss,
     update_rows_sampled,
 )

@@ -23,8 +23,14 @@ Conventions (per head): d = head width, h = hidden width.
   W2 [H, d, h].
 
 Readings taken where the pages leave a step open:
-  * one plain gradient step W - g (the Newton-Schulz orthonormalisation the
-    review mentions is not part of this path);
+  * one gradient step on the chunk; the step is W - g by default, or
+    W - NewtonSchulz(g) when asked for ([review] the update display after
+    Eq. (3)): the pages name the Muon optimizer's Newton-Schulz
+    orthonormalisation but give neither its polynomial nor its step count,
+    so the reading is Muon's published odd quintic iteration (K. Jordan,
+    "Muon: An optimizer for hidden layers in neural networks", 2024),
+    coefficients (3.4445, -4.7750, 2.0315), five steps, started from
+    g / max(||g||_F, 1e-12);
   * the chunk gradient is a sum over tokens, no 1/n;
   * eta is one scalar per token and head;
   * the optional renormalisation is per row (the fan-in vector of one output
@@ -38,6 +44,9 @@ import numpy as np
 
 TOKEN_BLOCK = 65536
 RENORM_EPS = 1e-12
+MUON_NS_COEFFS = (3.4445, -4.7750, 2.0315)
+NS_STEPS = 5
+STEP_RULES = ("gradient", "newton_schulz")
 
 
 def _f64(x):
@@ -165,6 +174,30 @@ def gradient_step(params, grads):
     return tuple(_f64(w) - _f64(g) for w, g in zip(params, grads))
 
 
+def newton_schulz(g, steps=NS_STEPS, coeffs=MUON_NS_COEFFS, eps=RENORM_EPS):
+    """Newton-Schulz orthonormalisation of one gradient matrix.
+
+    [review] the update display after Eq. (3): Delta <- NewtonSchulz(g),
+    following the Muon optimizer.  Each step applies the odd matrix
+    polynomial X <- a X + b (X X^T) X + c (X X^T)^2 X to
+    X_0 = g / max(||g||_F, eps); it maps every singular value s of X to
+    a s + b s^3 + c s^5 and keeps the singular vectors, so the result
+    approaches U V^T (g = U S V^T) for coefficients that drive the
+    normalised singular values towards 1 (the textbook cubic (1.5, -0.5, 0)
+    converges to U V^T exactly; Muon's quintic lands them near 1 in five
+    steps).  g = 0 gives 0.
+    """
+    x = _f64(g)
+    nrm = np.sqrt((x * x).sum())
+    x = x / max(nrm, eps)
+    a, b, c = coeffs
+    for _ in range(steps):
+        gram = x @ x.T
+        gx = gram @ x
+        x = a * x + b * gx + c * (gram @ gx)
+    return x
+
+
 def renorm_rows(w_old, w_new, eps=RENORM_EPS):
     """Norm-preserving L2 renormalisation of the updated weight.
 
@@ -181,11 +214,17 @@ def renorm_rows(w_old, w_new, eps=RENORM_EPS):
     return w_new * scale
 
 
-def update_head(k, v, eta, w1, w2, w3, renorm=False, block=None):
+def update_head(k, v, eta, w1, w2, w3, renorm=False, block=None, step="gradient"):
     """One head: W -> W_hat on one chunk of n tokens.
-    k, v: [n, d]; eta: [n]; returns (W1_hat, W2_hat, W3_hat)."""
+    k, v: [n, d]; eta: [n]; returns (W1_hat, W2_hat, W3_hat).
+    step = "gradient": W' = W - g;  step = "newton_schulz": W' = W -
+    NewtonSchulz(g) per matrix ([review] the update display after Eq. (3))."""
+    if step not in STEP_RULES:
+        raise ValueError(step)
     params = tuple(map(_f64, (w1, w2, w3)))
     grads = chunk_gradient(vjp_swiglu, params, k, v, eta, block=block)
+    if step == "newton_schulz":
+        grads = tuple(newton_schulz(g) for g in grads)
     new = gradient_step(params, grads)
     if renorm:
         new = tuple(renorm_rows(p, q) for p, q in zip(params, new))
@@ -212,7 +251,7 @@ def virtual_loss(k, v, eta, w1, w2, w3):
 # ---------------------------------------------------------------------------
 # Multi-head entry points (heads are independent fast weights)
 # ---------------------------------------------------------------------------
-def update(k, v, eta, w1, w2, w3, renorm=False, block=None):
+def update(k, v, eta, w1, w2, w3, renorm=False, block=None, step="gradient"):
     """All heads: k, v [n, H, d]; eta [n, H]; W1, W3 [H, h, d]; W2 [H, d, h].
     Returns float64 (W1_hat, W2_hat, W3_hat)."""
     k, v, eta = _f64(k), _f64(v), _f64(eta)
@@ -222,7 +261,7 @@ def update(k, v, eta, w1, w2, w3, renorm=False, block=None):
     for hd in range(heads):
         o1[hd], o2[hd], o3[hd] = update_head(
             k[:, hd], v[:, hd], eta[:, hd], w1[hd], w2[hd], w3[hd],
-            renorm=renorm, block=block)
+            renorm=renorm, block=block, step=step)
     return o1, o2, o3
 
 
@@ -236,15 +275,15 @@ def apply(q, w1, w2, w3, block=None):
     return out
 
 
-def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, block=None):
+def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, block=None, step="gradient"):
     """Bidirectional single chunk: update on all tokens, then read every
     query through the updated weights ([notes] write/read flow; [review]
     Eq. (3) then Eq. (4)).  Returns ((W1_hat, W2_hat, W3_hat), o)."""
-    new = update(k, v, eta, w1, w2, w3, renorm=renorm, block=block)
+    new = update(k, v, eta, w1, w2, w3, renorm=renorm, block=block, step=step)
     return new, apply(q, *new, block=block)
 
 
-def stream(frames, w1, w2, w3, renorm=False, order="apply_then_update"):
+def stream(frames, w1, w2, w3, renorm=False, order="apply_then_update", step="gradient"):
     """Streaming: W(t) = Update(W(t-1); frame t) frame after frame
     ([review] 3. Streaming Reconstruction, Eq. (6); [notes] 流式更新).
     Each frame is a dict with q, k, v [p, H, d] and eta [p, H].
@@ -260,11 +299,49 @@ def stream(frames, w1, w2, w3, renorm=False, order="apply_then_update"):
     for fr in frames:
         if order == "apply_then_update":
             outs.append(apply(fr["q"], *w))
-            w = update(fr["k"], fr["v"], fr["eta"], *w, renorm=renorm)
+            w = update(fr["k"], fr["v"], fr["eta"], *w, renorm=renorm, step=step)
         else:
-            w = update(fr["k"], fr["v"], fr["eta"], *w, renorm=renorm)
+            w = update(fr["k"], fr["v"], fr["eta"], *w, renorm=renorm, step=step)
             outs.append(apply(fr["q"], *w))
     return w, outs
+
+
+def chunked(q, k, v, eta, offsets, w1, w2, w3, order="update_then_apply", update_mask=None,
+            inner_steps=1, renorm=False, step="gradient"):
+    """A token sequence cut into consecutive chunks [offsets[c], offsets[c+1]),
+    read and written chunk after chunk ([lact] 3、应用场景, orders (b)-(d)):
+      order "update_then_apply" (block-causal, (b)): W <- Update(W; chunk c),
+            then o_c = f_W(q_c);
+      order "apply_then_update" (shifted block-causal, (c)): o_c = f_W(q_c),
+            then W <- Update(W; chunk c);
+      update_mask[c] False skips the update of chunk c, which is then only
+            read (selective update, (d): writes on some chunks, reads on all);
+      inner_steps > 1 repeats the update on the same chunk, each step taking
+            the gradient at the weights the previous step produced.
+    A per-chunk rate is a scaling of that chunk's eta rows.  q, k, v [n, H, d];
+    eta [n, H].  Returns (final weights, o [n, H, d_out])."""
+    if order not in ("apply_then_update", "update_then_apply"):
+        raise ValueError(order)
+    if inner_steps < 1:
+        raise ValueError(inner_steps)
+    offsets = [int(x) for x in offsets]
+    n_chunks = len(offsets) - 1
+    if n_chunks < 0 or offsets[0] != 0 or any(b < a for a, b in zip(offsets, offsets[1:])):
+        raise ValueError("offsets must start at 0 and not decrease")
+    mask = [True] * n_chunks if update_mask is None else [bool(m) for m in update_mask]
+    w = tuple(map(_f64, (w1, w2, w3)))
+    q = _f64(q)
+    out = np.zeros((q.shape[0], q.shape[1], w[1].shape[1]))
+    for c in range(n_chunks):
+        s, e = offsets[c], offsets[c + 1]
+        if order == "apply_then_update":
+            out[s:e] = apply(q[s:e], *w)
+        if mask[c]:
+            for _ in range(inner_steps):
+                w = update(k[s:e], v[s:e], eta[s:e], *w, renorm=renorm, step=step)
+        if order == "update_then_apply":
+            out[s:e] = apply(q[s:e], *w)
+    return w, out
 
 
 def update_rows_sampled(k, v, eta, w1, w2, w3, hidden_idx, block=None):
