@@ -83,13 +83,28 @@ typedef enum zm_renorm { ZM_RENORM_NONE = 0, ZM_RENORM_ROW = 1 } zm_renorm;
  * UPDATE_THEN_APPLY writes frame t first and reads it with W(t). */
 typedef enum zm_order { ZM_APPLY_THEN_UPDATE = 0, ZM_UPDATE_THEN_APPLY = 1 } zm_order;
 
+/* The step taken with the chunk gradient g of one weight matrix (review, the
+ * update display after Eq. (3)):
+ *   ZM_STEP_GRADIENT:      W' = W - g;
+ *   ZM_STEP_NEWTON_SCHULZ: W' = W - NewtonSchulz(g), the orthonormalisation of
+ *     the Muon optimizer that the review names.  The pages give neither its
+ *     polynomial nor its step count; the library runs Muon's published odd
+ *     quintic: five steps of X <- a X + b (X X^T) X + c (X X^T)^2 X with
+ *     (a, b, c) = (3.4445, -4.7750, 2.0315) from X = g / max(||g||_F, 1e-12),
+ *     per head and per matrix.  Its products run in split-bf16 (hi + lo
+ *     parts, three bf16 matrix-core products each, fp32 accumulation) with bf16
+ *     io and in fp32 with fp32 io.  The result no longer scales with eta: the
+ *     step has singular values near 1 whatever the gradient's size, so it is
+ *     meant to be used with ZM_RENORM_ROW.  n_kv = 0 leaves W unchanged. */
+typedef enum zm_step_rule { ZM_STEP_GRADIENT = 0, ZM_STEP_NEWTON_SCHULZ = 1 } zm_step_rule;
+
 typedef struct zm_ttt_desc {
   int32_t heads;      /* independent fast weights */
   int32_t d_head;     /* d: width of q, k, v, o per head */
   int32_t d_hidden;   /* h: SwiGLU hidden width */
   int32_t io_dtype;   /* zm_dtype of q, k, v, o */
   int32_t renorm;     /* zm_renorm */
-  int32_t reserved;   /* must be 0 */
+  int32_t step_rule;  /* zm_step_rule (0: plain gradient step) */
   int64_t ld_tok;     /* elements between consecutive tokens of q/k/v/o */
 } zm_ttt_desc;
 
@@ -99,7 +114,8 @@ typedef struct zm_ttt_desc {
 ZM_API int zm_ttt_workspace_size(const zm_ttt_desc* desc, int64_t n_kv, int64_t n_q, size_t* bytes);
 
 /* Update (review Eq. (2)-(3) and the renormalised update display):
- *   W' = W - grad_W sum_{i<n_kv} eta_i L(f_W(k_i), v_i),  L(f, v) = -f^T v,
+ *   g = grad_W sum_{i<n_kv} eta_i L(f_W(k_i), v_i),  L(f, v) = -f^T v,
+ *   W' = W - g  (or W - NewtonSchulz(g), see zm_step_rule),
  *   W_hat = renorm(W, W') if desc->renorm else W'.
  * k, v: [n_kv, heads, d_head] tokens; eta: [n_kv, heads].
  * w1, w2, w3: the current fast weights (read only).

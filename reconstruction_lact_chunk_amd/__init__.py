@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     OK,
     RENORM_NONE,
     RENORM_ROW,
+    STEP_GRADIENT,
+    STEP_NEWTON_SCHULZ,
     UPDATE_THEN_APPLY,
     Desc,
     ZmError,

@@ -18,6 +18,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 RENORM_NONE, RENORM_ROW = 0, 1
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
     "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
@@ -38,7 +39,7 @@ class Desc(ctypes.Structure):
         ("d_hidden", ctypes.c_int32),
         ("io_dtype", ctypes.c_int32),
         ("renorm", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("step_rule", ctypes.c_int32),
         ("ld_tok", ctypes.c_int64),
     ]
 
@@ -132,13 +133,14 @@ def _token_ld(x, heads, d, io):
     return x.stride(0) if x.shape[0] > 1 else heads * d
 
 
-def make_desc(w1, w2, w3, io_dtype: int, renorm: bool, *tokens) -> Desc:
+def make_desc(w1, w2, w3, io_dtype: int, renorm: bool, *tokens, step_rule: int = STEP_GRADIENT
+              ) -> Desc:
     heads, d, h = _check_weights(w1, w2, w3)
     lds = {_token_ld(x, heads, d, io_dtype) for x in tokens if x is not None and x.shape[0] > 1}
     if len(lds) > 1:
         raise ZmError("all token tensors of one call must share the token stride")
     ld = lds.pop() if lds else heads * d
-    return Desc(heads, d, h, io_dtype, RENORM_ROW if renorm else RENORM_NONE, 0, ld)
+    return Desc(heads, d, h, io_dtype, RENORM_ROW if renorm else RENORM_NONE, int(step_rule), ld)
 
 
 def _io_of(*tokens) -> int:
@@ -189,11 +191,12 @@ def _ws_bytes(ws):
 # ---------------------------------------------------------------------------
 # entry points
 # ---------------------------------------------------------------------------
-def update(k, v, eta, w1, w2, w3, renorm=False, out=None, workspace=None):
+def update(k, v, eta, w1, w2, w3, renorm=False, out=None, workspace=None,
+           step_rule=STEP_GRADIENT):
     """W_hat = step(W; k, v, eta) (+ row renorm).  Returns (W1_hat, W2_hat, W3_hat);
     pass out=(w1, w2, w3) to update in place."""
     io = _io_of(k, v)
-    desc = make_desc(w1, w2, w3, io, renorm, k, v)
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, step_rule=step_rule)
     n = k.shape[0]
     if v.shape[0] != n:
         raise ZmError("k and v token counts differ")
@@ -222,12 +225,13 @@ def apply(q, w1, w2, w3, out=None, workspace=None):
     return o
 
 
-def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, workspace=None):
+def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, workspace=None,
+                 step_rule=STEP_GRADIENT):
     """Bidirectional chunk: update on (k, v, eta), then o = f_{W_hat}(q).
     Returns ((W1_hat, W2_hat, W3_hat), o)."""
     io = _io_of(k, v, q)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o)
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o, step_rule=step_rule)
     n_kv, n_q = k.shape[0], q.shape[0]
     if v.shape[0] != n_kv:
         raise ZmError("k and v token counts differ")
@@ -243,12 +247,12 @@ def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, w
 
 
 def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE, out=None,
-                workspace=None):
+                workspace=None, step_rule=STEP_GRADIENT):
     """One frame of the streaming recursion; w1, w2, w3 are updated in place.
     Returns o (read with W(t-1) for APPLY_THEN_UPDATE, W(t) otherwise)."""
     io = _io_of(q, k, v)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o)
+    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule)
     n = q.shape[0]
     if k.shape[0] != n or v.shape[0] != n:
         raise ZmError("q, k and v of one frame must have the same token count")

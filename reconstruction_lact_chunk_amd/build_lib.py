@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzmttt.so")
 ARCH = "gfx950"
 
-SOURCES = ["weights.hip", "update_bf16.hip", "apply_bf16.hip", "fp32_path.hip", "api.cpp"]
+SOURCES = ["weights.hip", "update_bf16.hip", "apply_bf16.hip", "fp32_path.hip",
+           "newton_schulz.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",

@@ -39,7 +39,8 @@ int check_desc(const zm_ttt_desc* d) {
   if (d->heads < 1 || d->d_head < 1 || d->d_hidden < 1) return ZM_ERR_INVALID_ARG;
   if (d->io_dtype != ZM_BF16 && d->io_dtype != ZM_F32) return ZM_ERR_INVALID_ARG;
   if (d->renorm != ZM_RENORM_NONE && d->renorm != ZM_RENORM_ROW) return ZM_ERR_INVALID_ARG;
-  if (d->reserved != 0) return ZM_ERR_INVALID_ARG;
+  if (d->step_rule != ZM_STEP_GRADIENT && d->step_rule != ZM_STEP_NEWTON_SCHULZ)
+    return ZM_ERR_INVALID_ARG;
   if (d->ld_tok < (int64_t)d->heads * d->d_head || d->ld_tok % 8 != 0) return ZM_ERR_INVALID_ARG;
   if (d->heads > 64) return ZM_ERR_UNSUPPORTED;
   const bool ok_shape = (d->d_head == 64 || d->d_head == 128) &&
@@ -140,8 +141,15 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
     }
   }
   Scoped s(kStageReduce, st);
-  ZM_HIP(launch_reduce(part, L.plan.splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1, o2,
-                       o3, d->renorm, emit, st));
+  int splits = L.plan.splits;
+  if (n > 0 && d->step_rule == ZM_STEP_NEWTON_SCHULZ) {
+    // partials -> slot 0 -> NewtonSchulz(minus the gradient), in place
+    ZM_HIP(launch_newton_schulz(part, splits, d->heads, d->d_head, d->d_hidden,
+                                d->io_dtype == ZM_F32, st));
+    splits = 1;
+  }
+  ZM_HIP(launch_reduce(part, splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1, o2, o3,
+                       d->renorm, emit, st));
   return ZM_OK;
 }
 

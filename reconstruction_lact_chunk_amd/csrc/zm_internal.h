@@ -144,6 +144,11 @@ hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
                          const float* w1, const float* w2, const float* w3,
                          float* o1, float* o2, float* o3, int renorm, const WSet* out_bf16,
                          hipStream_t st);
+// Sums the split slots of part into slot 0 and replaces each matrix there by
+// its Newton-Schulz orthonormalisation (in place).  f32: fp32 products,
+// else split-bf16 products.
+hipError_t launch_newton_schulz(float* part, int splits, int heads, int d, int h, bool f32,
+                                hipStream_t st);
 
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
                              int d, int h, WSet w, hipStream_t st);

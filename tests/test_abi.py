@@ -48,8 +48,8 @@ def test_version_and_status_strings():
     assert zm.status_string(-99) == "unknown status"
 
 
-def desc(heads=8, d=128, h=256, io=zm.BF16, renorm=1, ld=None, reserved=0):
-    return zm.Desc(heads, d, h, io, renorm, reserved, heads * d if ld is None else ld)
+def desc(heads=8, d=128, h=256, io=zm.BF16, renorm=1, ld=None, step_rule=0):
+    return zm.Desc(heads, d, h, io, renorm, step_rule, heads * d if ld is None else ld)
 
 
 def ws_size(de, n_kv, n_q):
@@ -83,7 +83,8 @@ def test_workspace_size_structure():
     ("d_hidden", 0, zm.ERR_INVALID_ARG),
     ("io_dtype", 7, zm.ERR_INVALID_ARG),
     ("renorm", 2, zm.ERR_INVALID_ARG),
-    ("reserved", 1, zm.ERR_INVALID_ARG),
+    ("step_rule", 2, zm.ERR_INVALID_ARG),
+    ("step_rule", -1, zm.ERR_INVALID_ARG),
     ("ld_tok", 8 * 128 - 8, zm.ERR_INVALID_ARG),
     ("ld_tok", 8 * 128 + 4, zm.ERR_INVALID_ARG),
 ])
@@ -93,6 +94,11 @@ def test_bad_descriptor(field, value, expect):
     if field == "heads" and value > 0:
         de.ld_tok = value * de.d_head
     assert ws_size(de, 10, 10)[0] == expect
+
+
+@pytest.mark.parametrize("rule", [zm.STEP_GRADIENT, zm.STEP_NEWTON_SCHULZ])
+def test_step_rules_accepted_without_extra_workspace(rule):
+    assert ws_size(desc(step_rule=rule), 10_992, 10_992) == ws_size(desc(), 10_992, 10_992)
 
 
 def test_null_descriptor_and_counts():

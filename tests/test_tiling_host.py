@@ -10,6 +10,9 @@ barrier interval both writes and reads one LDS buffer or writes a buffer whose
 previous contents are still needed.
 """
 import itertools
+import math
+
+import numpy as np
 
 import pytest
 
@@ -407,3 +410,192 @@ def test_apply_tiles_conflict_free(D, H):
             # head width 64: 136-byte rows put two rows' pieces of one half-wave
             # on 34 slots of 32, so one pair collides (2-way); 128: conflict-free
             assert read_b64_degree(addrs) == (1 if D == 128 else 2)
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz kernel (newton_schulz.hip): a numpy model of its data movement
+# with the kernel's offset arithmetic, run in fp64.  It checks that every
+# global and LDS offset is in bounds, that each store phase writes distinct
+# elements, and that the five steps compute X <- a X + (b A + c A^2) X.
+# ---------------------------------------------------------------------------
+NS_COEFFS = (3.4445, -4.7750, 2.0315)
+
+
+def ns_cfg(M, N, pad):
+    PW = min(N, 128)
+    cfg = dict(PW=PW, NP=N // PW, RB=M // 64, CB1=M // 32, CB3=PW // 32,
+               PITCH_X=PW + pad, PITCH_XT=M + pad)
+    cfg["PLANE_P"] = max(M * cfg["PITCH_X"], PW * cfg["PITCH_XT"])
+    cfg["PLANE_Q"] = M * cfg["PITCH_XT"]
+    return cfg
+
+
+def _lanes():
+    for w in range(8):
+        for l in range(64):
+            yield w, l, l & 15, l >> 4
+
+
+def ns_model(x0, pad, kb, steps=5, tr=False):
+    """Emulates k_newton_schulz on one matrix x0 ([N][M] if tr else [M][N])."""
+    M, N = (x0.shape[1], x0.shape[0]) if tr else x0.shape
+    C = ns_cfg(M, N, pad)
+    PW, NP, RB, CB1, CB3 = C["PW"], C["NP"], C["RB"], C["CB1"], C["CB3"]
+    gflat = x0.reshape(-1).astype(float).copy()
+    lds_size = C["PLANE_P"] + C["PLANE_Q"]          # one plane of each region
+    lds = np.full(lds_size, np.nan)
+    QB = C["PLANE_P"]
+
+    def tile(w):
+        return (w >> 1) * 16 * RB, (w & 1) * 16 * CB1, (w & 1) * 16 * CB3
+
+    def gofs(i, j):
+        o = j * M + i if tr else i * N + j
+        assert 0 <= o < M * N
+        return o
+
+    # master X per lane: xm[(w, l)][p, rb, cb, ii]
+    xm = {}
+    seen = set()
+    for w, l, c, g in _lanes():
+        r0, _, c03 = tile(w)
+        a = np.zeros((NP, RB, CB3, 4))
+        for p in range(NP):
+            for rb in range(RB):
+                for cb in range(CB3):
+                    for ii in range(4):
+                        i, j = r0 + 16 * rb + 4 * g + ii, p * PW + c03 + 16 * cb + c
+                        o = gofs(i, j)
+                        assert o not in seen
+                        seen.add(o)
+                        a[p, rb, cb, ii] = gflat[o]
+        xm[(w, l)] = a
+    assert len(seen) == M * N
+    nrm = math.sqrt(sum(float((v * v).sum()) for v in xm.values()))
+    for k in xm:
+        xm[k] /= max(nrm, 1e-12)
+
+    def store(off, val, region_lo, region_hi, written):
+        assert region_lo <= off < region_hi and off not in written
+        written.add(off)
+        lds[off] = val
+
+    def product(RBc, CBc, K, s1, pitch1, s2, pitch2, c0sel):
+        """acc[(w,l)][rb, cb, ii] = sum_k S1[row][k] S2[col][k] per MFMA layout."""
+        kof = kb // 4
+        kidx = np.array([k0 + kof * gg + e for k0 in range(0, K, kb) for gg in range(4)
+                         for e in range(kof)])
+        assert sorted(kidx.tolist()) == list(range(K))
+        acc = {}
+        for w, l, c, g in _lanes():
+            r0, c01, c03 = tile(w)
+            c0 = c01 if c0sel == 1 else c03
+            out = np.zeros((RBc, CBc, 4))
+            for rb in range(RBc):
+                for cb in range(CBc):
+                    for ii in range(4):
+                        row = 4 * g + ii       # D row within the block
+                        # contraction offsets: fragment steps k0, lane groups gg
+                        # (each supplying kof consecutive elements)
+                        oa = s1 + (r0 + 16 * rb + row) * pitch1 + kidx
+                        ob = s2 + (c0 + 16 * cb + c) * pitch2 + kidx
+                        assert oa.min() >= 0 and oa.max() < lds_size
+                        assert ob.min() >= 0 and ob.max() < lds_size
+                        out[rb, cb, ii] = float(lds[oa] @ lds[ob])
+            acc[(w, l)] = out
+        return acc
+
+    def store_t(dst, pitch, acc, RBc, CBc, c0sel, lo, hi):
+        written = set()
+        for w, l, c, g in _lanes():
+            r0, c01, c03 = tile(w)
+            c0 = c01 if c0sel == 1 else c03
+            for rb in range(RBc):
+                for cb in range(CBc):
+                    for ii in range(4):
+                        off = dst + (c0 + 16 * cb + c) * pitch + r0 + 16 * rb + 4 * g + ii
+                        store(off, acc[(w, l)][rb, cb, ii], lo, hi, written)
+        return written
+
+    a_, b_, c_ = NS_COEFFS
+    for _ in range(steps):
+        acc_a = None
+        for p in range(NP):
+            lds[:QB] = np.nan
+            written = set()
+            for w, l, c, g in _lanes():
+                r0, _, c03 = tile(w)
+                for rb in range(RB):
+                    for cb in range(CB3):
+                        for ii in range(4):
+                            off = (r0 + 16 * rb + 4 * g + ii) * C["PITCH_X"] + c03 + 16 * cb + c
+                            store(off, xm[(w, l)][p, rb, cb, ii], 0, QB, written)
+            assert len(written) == M * PW
+            part = product(RB, CB1, PW, 0, C["PITCH_X"], 0, C["PITCH_X"], 1)
+            acc_a = part if acc_a is None else {k: acc_a[k] + part[k] for k in part}
+        lds[QB:] = np.nan
+        assert len(store_t(QB, C["PITCH_XT"], acc_a, RB, CB1, 1, QB, lds_size)) == M * M
+        acc_c = product(RB, CB1, M, QB, C["PITCH_XT"], QB, C["PITCH_XT"], 1)
+        # A read back from its transposed store at the same offsets
+        acc_b = {}
+        for w, l, c, g in _lanes():
+            r0, c01, _ = tile(w)
+            back = np.zeros((RB, CB1, 4))
+            for rb in range(RB):
+                for cb in range(CB1):
+                    for ii in range(4):
+                        back[rb, cb, ii] = lds[QB + (c01 + 16 * cb + c) * C["PITCH_XT"] + r0
+                                               + 16 * rb + 4 * g + ii]
+            np.testing.assert_array_equal(back, acc_a[(w, l)])
+            acc_b[(w, l)] = b_ * back + c_ * acc_c[(w, l)]
+        lds[QB:] = np.nan
+        store_t(QB, C["PITCH_XT"], acc_b, RB, CB1, 1, QB, lds_size)
+        for p in range(NP):
+            lds[:QB] = np.nan
+            sub = {k: v[p] for k, v in xm.items()}
+            assert len(store_t(0, C["PITCH_XT"], sub, RB, CB3, 3, 0, QB)) == M * PW
+            prod = product(RB, CB3, M, QB, C["PITCH_XT"], 0, C["PITCH_XT"], 3)
+            for k in xm:
+                xm[k][p] = a_ * xm[k][p] + prod[k]
+    out = np.zeros(M * N)
+    for w, l, c, g in _lanes():
+        r0, _, c03 = tile(w)
+        for p in range(NP):
+            for rb in range(RB):
+                for cb in range(CB3):
+                    for ii in range(4):
+                        out[gofs(r0 + 16 * rb + 4 * g + ii, p * PW + c03 + 16 * cb + c)] = \
+                            xm[(w, l)][p, rb, cb, ii]
+    return out.reshape(x0.shape), C
+
+
+def _ns_plain(x, steps=5):
+    a, b, c = NS_COEFFS
+    x = x / max(np.linalg.norm(x), 1e-12)
+    for _ in range(steps):
+        A = x @ x.T
+        x = a * x + (b * A + c * A @ A) @ x
+    return x
+
+
+@pytest.mark.parametrize("M,N", [(64, 128), (64, 256), (128, 128), (128, 256)])
+@pytest.mark.parametrize("pad,kb,elem,lds_limit", [(16, 32, 2, 160 * 1024), (8, 16, 4, 160 * 1024)])
+def test_newton_schulz_kernel_data_movement(M, N, pad, kb, elem, lds_limit):
+    r = np.random.default_rng(M + N)
+    C = ns_cfg(M, N, pad)
+    planes = 2 if elem == 2 else 1
+    assert planes * (C["PLANE_P"] + C["PLANE_Q"]) * elem + 32 <= lds_limit
+    x = r.normal(size=(M, N))
+    steps = 2
+    got, _ = ns_model(x, pad, kb, steps=steps)
+    np.testing.assert_allclose(got, _ns_plain(x, steps), rtol=0, atol=1e-12)
+    if N > M:   # the W1 / W3 orientation: [N][M] in memory, X = G^T
+        got_t, _ = ns_model(x.T.copy(), pad, kb, steps=1, tr=True)
+        np.testing.assert_allclose(got_t, _ns_plain(x, 1).T, rtol=0, atol=1e-12)
+
+
+def test_newton_schulz_fragment_reads_conflict_free():
+    for el, pad in [(2, 16), (4, 8)]:
+        for K in (64, 128):
+            pitch = (K + pad) * el
+            assert read_b128_degree([(l % 16) * pitch + (l // 16) * 16 for l in range(64)]) == 1
