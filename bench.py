@@ -12,6 +12,7 @@ time from HIP events recorded by the library around that kernel on its own
 stream) and the fp64 oracle timed on a bounded sample on this host's cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload f700]
+                  [--step-rule gradient|newton_schulz]
                   [--cpu-sample-tokens N | --no-cpu-baseline]
 """
 from __future__ import annotations
@@ -47,6 +48,8 @@ def parse():
     p.add_argument("--cpu-sample-tokens", type=int, default=262144)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-renorm", action="store_true")
+    p.add_argument("--step-rule", default="gradient", choices=["gradient", "newton_schulz"],
+                   help="the update's step: W - g (default) or W - NewtonSchulz(g)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a known-size "
                         "reference dispatch for scaling HBM counters)")
@@ -81,7 +84,7 @@ def make_events(torch, n):
     return evs
 
 
-def cpu_baseline(inputs_host, sample_tokens, renorm):
+def cpu_baseline(inputs_host, sample_tokens, renorm, step_rule="gradient"):
     """The fp64 oracle (as it stands) on the first `sample_tokens` tokens."""
     import numpy as np
     import oracle
@@ -92,7 +95,8 @@ def cpu_baseline(inputs_host, sample_tokens, renorm):
         cores = os.cpu_count() or 1
     x = {k: v.astype(np.float64) if k in ("w1", "w2", "w3") else v for k, v in inputs_host.items()}
     t0 = time.perf_counter()
-    oracle.update_apply(x["k"], x["v"], x["eta"], x["q"], x["w1"], x["w2"], x["w3"], renorm=renorm)
+    oracle.update_apply(x["k"], x["v"], x["eta"], x["q"], x["w1"], x["w2"], x["w3"], renorm=renorm,
+                        step=step_rule)
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of the workload, all heads, update+apply "
@@ -118,6 +122,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = WL.WORKLOADS[args.workload]
     renorm = not args.no_renorm and wl.renorm
+    rule = zm.STEP_NEWTON_SCHULZ if args.step_rule == "newton_schulz" else zm.STEP_GRADIENT
     log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
         f"h={wl.d_hidden} layers={wl.layers}")
     if args.copy_calibration_mib > 0:
@@ -136,7 +141,7 @@ def main():
                      for i in range(wl.layers)]
     else:
         ws_layers = [tuple(layers)]
-    desc = zm.make_desc(x["w1"], x["w2"], x["w3"], zm.BF16, renorm, x["q"], x["k"])
+    desc = zm.make_desc(x["w1"], x["w2"], x["w3"], zm.BF16, renorm, x["q"], x["k"], step_rule=rule)
     if wl.streaming:
         p = wl.tokens_per_frame
         n_ws = zm.workspace_size(desc, p, p)
@@ -152,13 +157,13 @@ def main():
             w = [t.clone() for t in ws_layers[0]]
             for (s, e) in WL.frame_slices(wl):
                 zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
-                               renorm=renorm, out=o[s:e], workspace=ws)
+                               renorm=renorm, out=o[s:e], workspace=ws, step_rule=rule)
             return
         for li, wl_w in enumerate(ws_layers):
             if prof is not None:
                 zm.set_profile_events(prof[li])
             zm.update_apply(x["k"], x["v"], x["eta"], x["q"], *wl_w, renorm=renorm,
-                            w_out=w_out[li], out=o, workspace=ws)
+                            w_out=w_out[li], out=o, workspace=ws, step_rule=rule)
         if prof is not None:
             zm.set_profile_events(None)
 
@@ -169,7 +174,7 @@ def main():
     K = args.steps
     prof = None
     if not wl.streaming:
-        prof = [[make_events(torch, 8) for _ in ws_layers] for _ in range(K)]
+        prof = [[make_events(torch, 10) for _ in ws_layers] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -209,6 +214,8 @@ def main():
                                                / PEAK_BF16_TFLOPS, 4)
         # per-kernel durations from the library's event hooks
         names = {1: "update", 2: "reduce", 3: "apply", 0: "cast"}
+        if rule == zm.STEP_NEWTON_SCHULZ:
+            names[4] = "newton_schulz"
         durs = {nm: [] for nm in names.values()}
         for k in range(K):
             for li in range(len(ws_layers)):
@@ -225,6 +232,14 @@ def main():
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
         kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
         kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}
+        if "newton_schulz" in avg:
+            # five quintic steps per matrix: 4 M^2 N + 2 M^3 flops each (M = d, N = h)
+            m, nn = wl.d_head, wl.d_hidden
+            ns_flops = 3 * wl.heads * 5 * (4 * m * m * nn + 2 * m ** 3)
+            kern["newton_schulz"] = {
+                "avg_ms": round(avg["newton_schulz"], 4),
+                "achieved_tflops": round(ns_flops / (avg["newton_schulz"] / 1e3) / 1e12, 2),
+                "workgroups": 3 * wl.heads}
         dom = max(("update", "apply"), key=lambda nm: avg[nm])
         fl_dom = units[dom][0]
         ach = fl_dom / (avg[dom] / 1e3) / 1e12
@@ -245,6 +260,7 @@ def main():
         "n_kv": wl.n_kv, "n_q": wl.n_q, "heads": wl.heads, "d_head": wl.d_head,
         "d_hidden": wl.d_hidden, "layers": wl.layers, "renorm": renorm,
         "io": "bf16 tokens, fp32 fast weights, fp32 accumulation",
+        "step_rule": args.step_rule,
     }
     result["wall_s_timed"] = round(wall, 3)
 
@@ -254,7 +270,7 @@ def main():
         for k in ("w1", "w2", "w3"):
             host[k] = x[k].cpu().double().numpy()
         log(f"cpu baseline: oracle on {ns} tokens")
-        result["cpu_baseline"] = cpu_baseline(host, ns, renorm)
+        result["cpu_baseline"] = cpu_baseline(host, ns, renorm, args.step_rule)
     print(json.dumps(result), flush=True)
 
 

@@ -162,11 +162,12 @@ ZM_API const char* zm_status_string(int status);
 ZM_API int zm_ttt_version(void);
 
 /* Profiling aid: when events != NULL, every later launch of kernel stage s
- * (0 weight cast, 1 update partial sums, 2 reduce/step/renorm, 3 apply)
- * records events[2s] before and events[2s+1] after itself on the launch
- * stream, for each non-NULL slot.  The events are hipEvent_t handles passed
- * as void*; n_events must be 8 (or 0 with events == NULL to switch off).
- * Process-wide setting; not for concurrent use from several threads. */
+ * (0 weight cast, 1 update partial sums, 2 reduce/step/renorm, 3 apply,
+ * 4 Newton-Schulz) records events[2s] before and events[2s+1] after itself on
+ * the launch stream, for each non-NULL slot.  The events are hipEvent_t
+ * handles passed as void*; n_events must be 8 (stages 0-3) or 10 (or 0 with
+ * events == NULL to switch off).  Process-wide setting; not for concurrent use
+ * from several threads. */
 ZM_API int zm_ttt_set_profile_events(void* const* events, int n_events);
 
 #ifdef __cplusplus

@@ -266,15 +266,16 @@ def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE,
 
 
 def set_profile_events(events):
-    """events: 8 torch.cuda.Event (or None entries) recorded around the four
-    kernel stages (cast, update partials, reduce, apply); None switches off."""
+    """events: 8 or 10 torch.cuda.Event (or None entries) recorded around the
+    kernel stages (cast, update partials, reduce, apply, Newton-Schulz); None
+    switches off."""
     lib = load_library()
     if events is None:
         _check(lib.zm_ttt_set_profile_events(None, 0), "zm_ttt_set_profile_events")
         return
-    if len(events) != 8:
-        raise ZmError("need 8 event slots")
-    arr = (ctypes.c_void_p * 8)()
+    if len(events) not in (8, 10):
+        raise ZmError("need 8 or 10 event slots")
+    arr = (ctypes.c_void_p * len(events))()
     for i, e in enumerate(events):
         arr[i] = None if e is None else ctypes.c_void_p(int(e.cuda_event))
-    _check(lib.zm_ttt_set_profile_events(arr, 8), "zm_ttt_set_profile_events")
+    _check(lib.zm_ttt_set_profile_events(arr, len(events)), "zm_ttt_set_profile_events")

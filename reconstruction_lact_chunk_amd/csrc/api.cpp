@@ -14,10 +14,17 @@ namespace {
 
 constexpr int kVersion = 10000;  // 1.0.0
 
-void* g_prof[8] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+constexpr int kMaxProfEvents = 10;
+void* g_prof[kMaxProfEvents] = {};
 bool g_prof_on = false;
 
-enum Stage { kStageCast = 0, kStageUpdate = 1, kStageReduce = 2, kStageApply = 3 };
+enum Stage {
+  kStageCast = 0,
+  kStageUpdate = 1,
+  kStageReduce = 2,
+  kStageApply = 3,
+  kStageNewtonSchulz = 4
+};
 
 inline void prof_mark(int slot, hipStream_t st) {
   if (g_prof_on && g_prof[slot]) (void)hipEventRecord((hipEvent_t)g_prof[slot], st);
@@ -140,14 +147,15 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
                                d->d_head, d->d_hidden, w1, w2, w3, part, L.plan, st));
     }
   }
-  Scoped s(kStageReduce, st);
   int splits = L.plan.splits;
   if (n > 0 && d->step_rule == ZM_STEP_NEWTON_SCHULZ) {
     // partials -> slot 0 -> NewtonSchulz(minus the gradient), in place
+    Scoped ns(kStageNewtonSchulz, st);
     ZM_HIP(launch_newton_schulz(part, splits, d->heads, d->d_head, d->d_hidden,
                                 d->io_dtype == ZM_F32, st));
     splits = 1;
   }
+  Scoped s(kStageReduce, st);
   ZM_HIP(launch_reduce(part, splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1, o2, o3,
                        d->renorm, emit, st));
   return ZM_OK;
@@ -189,12 +197,12 @@ const char* zm_status_string(int status) {
 int zm_ttt_set_profile_events(void* const* events, int n_events) {
   if (events == nullptr) {
     if (n_events != 0) return ZM_ERR_INVALID_ARG;
-    for (int i = 0; i < 8; ++i) g_prof[i] = nullptr;
+    for (int i = 0; i < kMaxProfEvents; ++i) g_prof[i] = nullptr;
     g_prof_on = false;
     return ZM_OK;
   }
-  if (n_events != 8) return ZM_ERR_INVALID_ARG;
-  for (int i = 0; i < 8; ++i) g_prof[i] = events[i];
+  if (n_events != 8 && n_events != kMaxProfEvents) return ZM_ERR_INVALID_ARG;
+  for (int i = 0; i < kMaxProfEvents; ++i) g_prof[i] = i < n_events ? events[i] : nullptr;
   g_prof_on = true;
   return ZM_OK;
 }

@@ -163,9 +163,11 @@ def test_apply_update_apply_stream_reject_bad_arguments():
 def test_profile_event_argument_checks():
     L = lib()
     assert L.zm_ttt_set_profile_events(None, 3) == zm.ERR_INVALID_ARG
-    arr = (ctypes.c_void_p * 8)()
+    arr = (ctypes.c_void_p * 10)()
     assert L.zm_ttt_set_profile_events(arr, 4) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_set_profile_events(arr, 9) == zm.ERR_INVALID_ARG
     assert L.zm_ttt_set_profile_events(arr, 8) == zm.OK
+    assert L.zm_ttt_set_profile_events(arr, 10) == zm.OK
     assert L.zm_ttt_set_profile_events(None, 0) == zm.OK
 
 
