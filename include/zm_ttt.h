@@ -155,6 +155,31 @@ ZM_API int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_fram
                        float* w1, float* w2, float* w3, void* o,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/* A sequence of n = offsets[n_chunks] tokens cut into consecutive chunks
+ * [offsets[c], offsets[c+1]), read and written chunk after chunk with the
+ * orders of the LaCT summary (mhpn.cn, part 二, 3、应用场景):
+ *   ZM_UPDATE_THEN_APPLY: block-causal, W <- Update(W; chunk c), then
+ *     o_c = f_W(q_c) (order (b));
+ *   ZM_APPLY_THEN_UPDATE: shifted block-causal, o_c = f_W(q_c), then
+ *     W <- Update(W; chunk c) (order (c)).
+ * update_mask (host memory, n_chunks bytes, or NULL for all): a zero entry
+ * skips chunk c's update, so that chunk is only read (updates on selected
+ * chunks and reads on all, order (d)).  inner_steps (1..64) repeats the
+ * update on the same chunk, each step taking the gradient at the weights the
+ * previous one produced.  A per-chunk rate is a scaling of that chunk's eta
+ * rows.
+ * offsets: host memory, n_chunks + 1 int64, offsets[0] = 0, non-decreasing;
+ * n_chunks in [0, 2^24].  Empty chunks are skipped.
+ * q, k, v, o: [n, heads, d_head]; eta: [n, heads].  w1, w2, w3 hold the state
+ * and are updated in place.  The workspace must hold
+ * zm_ttt_workspace_size(desc, L, L) bytes, L the longest chunk.  Equivalent to
+ * one zm_ttt_stream_step per chunk (extended by the mask and inner steps). */
+ZM_API int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks,
+                   const int64_t* offsets, const uint8_t* update_mask, int inner_steps,
+                   const void* q, const void* k, const void* v, const float* eta,
+                   float* w1, float* w2, float* w3, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 ZM_API const char* zm_status_string(int status);
 

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     Desc,
     ZmError,
     apply,
+    chunked,
     load_library,
     make_desc,
     set_profile_events,

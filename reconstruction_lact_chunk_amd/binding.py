@@ -22,7 +22,8 @@ STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
     "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-    "zm_ttt_stream_step", "zm_status_string", "zm_ttt_version", "zm_ttt_set_profile_events",
+    "zm_ttt_stream_step", "zm_ttt_chunked", "zm_status_string", "zm_ttt_version",
+    "zm_ttt_set_profile_events",
 )
 
 
@@ -68,12 +69,15 @@ def load_library(path: str | None = None):
                                         _P, _P, _SZ, _P]
     lib.zm_ttt_stream_step.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _SZ, _P]
+    lib.zm_ttt_chunked.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, ctypes.c_int, _P, _P, _P,
+                                   _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.zm_status_string.argtypes = [ctypes.c_int]
     lib.zm_status_string.restype = ctypes.c_char_p
     lib.zm_ttt_version.argtypes = []
     lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
     for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-                 "zm_ttt_stream_step", "zm_ttt_version", "zm_ttt_set_profile_events"):
+                 "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_version",
+                 "zm_ttt_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -262,6 +266,38 @@ def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE,
                                            _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2), _ptr(w3),
                                            _ptr(o), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
     _check(st, "zm_ttt_stream_step")
+    return o
+
+
+def chunked(q, k, v, eta, offsets, w1, w2, w3, renorm=False, order=UPDATE_THEN_APPLY,
+            update_mask=None, inner_steps=1, out=None, workspace=None, step_rule=STEP_GRADIENT):
+    """A sequence cut into chunks [offsets[c], offsets[c+1]) read and written
+    chunk after chunk; w1, w2, w3 are updated in place.  update_mask: a
+    sequence of n_chunks booleans (False: read only).  Returns o."""
+    io = _io_of(q, k, v)
+    o = out if out is not None else _like_tokens(q)
+    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule)
+    offs = [int(x) for x in offsets]
+    n_chunks = len(offs) - 1
+    if n_chunks < 0:
+        raise ZmError("offsets needs at least one entry")
+    n = offs[-1]
+    if q.shape[0] != n or k.shape[0] != n or v.shape[0] != n:
+        raise ZmError(f"q, k, v must hold offsets[-1] = {n} tokens")
+    _eta(eta, n, desc.heads)
+    longest = max([b - a for a, b in zip(offs, offs[1:])] + [0])
+    ws, _ = _workspace(desc, longest, longest, w1.device, workspace)
+    off_arr = (ctypes.c_int64 * len(offs))(*offs)
+    mask_arr = None
+    if update_mask is not None:
+        if len(update_mask) != n_chunks:
+            raise ZmError("update_mask needs one entry per chunk")
+        mask_arr = (ctypes.c_uint8 * max(n_chunks, 1))(*[1 if m else 0 for m in update_mask])
+    st = load_library().zm_ttt_chunked(
+        ctypes.byref(desc), int(order), n_chunks, off_arr, mask_arr, int(inner_steps), _ptr(q),
+        _ptr(k), _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2), _ptr(w3), _ptr(o), _ptr(ws),
+        _ws_bytes(ws), _stream(w1.device))
+    _check(st, "zm_ttt_chunked")
     return o
 
 

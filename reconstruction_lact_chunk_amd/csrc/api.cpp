@@ -12,7 +12,9 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
+constexpr int64_t kMaxChunks = (int64_t)1 << 24;
+constexpr int kMaxInnerSteps = 64;
 
 constexpr int kMaxProfEvents = 10;
 void* g_prof[kMaxProfEvents] = {};
@@ -177,6 +179,39 @@ int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const flo
   return ZM_OK;
 }
 
+// One chunk of a sequence read and written in the given order (streaming
+// frame or chunk of zm_ttt_chunked): with APPLY_THEN_UPDATE o = f_W(q), then
+// W <- Update(W; chunk) `inner` times; with UPDATE_THEN_APPLY the updates come
+// first.  do_update = false only reads.  W is updated in place.
+int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_t n,
+              const void* q, const void* k, const void* v, const float* eta, float* w1, float* w2,
+              float* w3, void* o, void* ws, hipStream_t st) {
+  const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
+  const Layout L = layout(d, n);
+  const WSet a = carve_set(ws, L.set_a, welems);
+  const WSet b = carve_set(ws, L.set_b, welems);
+  const bool bf16 = d->io_dtype == ZM_BF16;
+  const int updates = do_update ? inner : 0;
+  if (order == ZM_APPLY_THEN_UPDATE || updates == 0) {
+    // Read the chunk with the incoming W; the first update shares that cast.
+    if (bf16) {
+      Scoped s(kStageCast, st);
+      ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
+    }
+    ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, st));
+    for (int i = 0; i < updates; ++i)
+      ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws, nullptr, bf16 && i == 0, st));
+    return ZM_OK;
+  }
+  // The last update also writes the bf16 copies the read uses.
+  for (int i = 0; i < updates; ++i)
+    ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws,
+                      (bf16 && n > 0 && i == updates - 1) ? &b : nullptr, false, st));
+  return run_apply(d, n, q, o, w1, w2, w3, b, st);
+}
+
+inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2 : 4; }
+
 }  // namespace
 
 extern "C" {
@@ -292,25 +327,49 @@ int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, cons
   ZM_TRY(check_tokens(o, n_frame));
   ZM_TRY(check_weights(w1, w2, w3));
   ZM_TRY(check_ws(desc, n_frame, workspace, workspace_bytes));
-  hipStream_t st = (hipStream_t)stream;
-  const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
-  const Layout L = layout(desc, n_frame);
-  const WSet a = carve_set(workspace, L.set_a, welems);
-  const WSet b = carve_set(workspace, L.set_b, welems);
-  const bool bf16 = desc->io_dtype == ZM_BF16;
-  if (order == ZM_APPLY_THEN_UPDATE) {
-    // Read the frame with W(t-1), then write it; both use one bf16 cast.
-    if (bf16) {
-      Scoped s(kStageCast, st);
-      ZM_HIP(launch_cast(w1, w2, w3, desc->heads, desc->d_head, desc->d_hidden, a, st));
+  return run_chunk(desc, order, true, 1, n_frame, q, k, v, eta, w1, w2, w3, o, workspace,
+                   (hipStream_t)stream);
+}
+
+int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const int64_t* offsets,
+                   const uint8_t* update_mask, int inner_steps, const void* q, const void* k,
+                   const void* v, const float* eta, float* w1, float* w2, float* w3, void* o,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  ZM_TRY(check_desc(desc));
+  if (order != ZM_APPLY_THEN_UPDATE && order != ZM_UPDATE_THEN_APPLY) return ZM_ERR_INVALID_ARG;
+  if (n_chunks < 0 || n_chunks > kMaxChunks) return ZM_ERR_INVALID_ARG;
+  if (inner_steps < 1 || inner_steps > kMaxInnerSteps) return ZM_ERR_INVALID_ARG;
+  if (n_chunks > 0 && !offsets) return ZM_ERR_INVALID_ARG;
+  int64_t longest = 0;
+  if (n_chunks > 0) {
+    if (offsets[0] != 0) return ZM_ERR_INVALID_ARG;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      const int64_t len = offsets[c + 1] - offsets[c];
+      if (len < 0) return ZM_ERR_INVALID_ARG;
+      if (len > longest) longest = len;
     }
-    ZM_TRY(run_apply(desc, n_frame, q, o, w1, w2, w3, a, st));
-    return run_update(desc, n_frame, k, v, eta, w1, w2, w3, w1, w2, w3, workspace, nullptr,
-                      true, st);
   }
-  ZM_TRY(run_update(desc, n_frame, k, v, eta, w1, w2, w3, w1, w2, w3, workspace,
-                    (bf16 && n_frame > 0) ? &b : nullptr, false, st));
-  return run_apply(desc, n_frame, q, o, w1, w2, w3, b, st);
+  const int64_t n = n_chunks > 0 ? offsets[n_chunks] : 0;
+  ZM_TRY(check_counts(n, n));
+  ZM_TRY(check_tokens(q, n));
+  ZM_TRY(check_tokens(k, n));
+  ZM_TRY(check_tokens(v, n));
+  ZM_TRY(check_eta(eta, n));
+  ZM_TRY(check_tokens(o, n));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_ws(desc, longest, workspace, workspace_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  const size_t row = (size_t)desc->ld_tok * io_bytes(desc);  // bytes per token row
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const int64_t s0 = offsets[c], len = offsets[c + 1] - s0;
+    if (len == 0) continue;  // nothing to read; an update on no tokens is the identity
+    const size_t tok = (size_t)s0 * row;
+    const bool upd = update_mask == nullptr || update_mask[c] != 0;
+    ZM_TRY(run_chunk(desc, order, upd, inner_steps, len, (const char*)q + tok,
+                     (const char*)k + tok, (const char*)v + tok, eta + s0 * desc->heads, w1, w2,
+                     w3, (char*)o + tok, workspace, st));
+  }
+  return ZM_OK;
 }
 
 }  // extern "C"

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10000
+    assert zm.version() == 10100
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -158,6 +158,39 @@ def test_apply_update_apply_stream_reject_bad_arguments():
                                     GOOD, GOOD, GOOD, GOOD, need, None) == zm.ERR_INVALID_ARG
     assert L.zm_ttt_stream_step(ctypes.byref(de), 0, 100, GOOD, GOOD, GOOD, None, GOOD, GOOD,
                                 GOOD, GOOD, GOOD, need, None) == zm.ERR_INVALID_ARG
+
+
+def call_chunked(de, offsets, order=0, mask=None, inner=1, q=GOOD, eta=GOOD, ws_bytes=0,
+                 n_chunks=None):
+    offs = None if offsets is None else (ctypes.c_int64 * len(offsets))(*offsets)
+    nc = (len(offsets) - 1 if offsets is not None else 1) if n_chunks is None else n_chunks
+    m = None if mask is None else (ctypes.c_uint8 * len(mask))(*mask)
+    return lib().zm_ttt_chunked(ctypes.byref(de), order, nc, offs, m, inner, q, GOOD, GOOD, eta,
+                                GOOD, GOOD, GOOD, GOOD, GOOD, ws_bytes, None)
+
+
+def test_chunked_rejects_bad_schedules_before_any_hip_call():
+    de = desc()
+    need = ws_size(de, 600, 600)[1]        # the longest chunk below has 600 tokens
+    good = [0, 400, 1000, 1200]
+    assert call_chunked(de, good, order=2, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, inner=0, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, inner=65, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, [5, 400, 1000], ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, [0, 400, 300], ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, n_chunks=-1, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, n_chunks=(1 << 24) + 1, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, q=None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_chunked(de, good, eta=P((1 << 20) + 2), ws_bytes=need) == zm.ERR_INVALID_ARG
+    # the workspace is sized by the longest chunk, not the whole sequence
+    short = ws_size(de, 599, 599)[1]
+    if short < need:
+        assert call_chunked(de, good, ws_bytes=short) == zm.ERR_WORKSPACE
+    assert call_chunked(desc(d=48), good, ws_bytes=need) == zm.ERR_UNSUPPORTED
+    # no chunks, or only empty ones: valid and nothing to launch
+    assert call_chunked(de, [0], ws_bytes=ws_size(de, 0, 0)[1]) == zm.OK
+    assert call_chunked(de, [0, 0, 0], q=None, eta=None, ws_bytes=ws_size(de, 0, 0)[1]) == zm.OK
 
 
 def test_profile_event_argument_checks():
