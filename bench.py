@@ -43,9 +43,11 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="f700",
-                   choices=["f700", "f100", "f8", "f700x24", "stream256"])
+                   choices=["f700", "f100", "f8", "f700x24", "stream256", "fw8", "fw100", "fw700"])
     p.add_argument("--seed", type=int, default=4)
-    p.add_argument("--cpu-sample-tokens", type=int, default=262144)
+    p.add_argument("--cpu-sample-tokens", type=int, default=0,
+                   help="tokens for the oracle baseline (default: 262144 at the 8-head shape, "
+                        "131072 at the full-width shape; 10-15 s of host time either way)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-renorm", action="store_true")
     p.add_argument("--step-rule", default="gradient", choices=["gradient", "newton_schulz"],
@@ -121,6 +123,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = WL.WORKLOADS[args.workload]
+    wide = wl.d_head == 1024
     renorm = not args.no_renorm and wl.renorm
     rule = zm.STEP_NEWTON_SCHULZ if args.step_rule == "newton_schulz" else zm.STEP_GRADIENT
     log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
@@ -230,6 +233,10 @@ def main():
             ach = fl / (avg[nm] / 1e3) / 1e12
             kern[nm] = {"avg_ms": round(avg[nm], 4), "achieved_tflops": round(ach, 1),
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        if wide:
+            for nm in ("update", "apply"):
+                kern[nm]["what"] = ("per 65,536-token block: hipBLASLt GEMMs (bf16, fp32 "
+                                    "accumulation) and the wide gate kernel")
         kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
         kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}
         if "newton_schulz" in avg:
@@ -243,11 +250,16 @@ def main():
         dom = max(("update", "apply"), key=lambda nm: avg[nm])
         fl_dom = units[dom][0]
         ach = fl_dom / (avg[dom] / 1e3) / 1e12
+        if wide:
+            kname = ("update stage (hipBLASLt GEMMs + k_wide_gate_update)" if dom == "update"
+                     else "apply stage (hipBLASLt GEMMs + k_wide_gate_apply)")
+        else:
+            kname = "k_update_bf16<128,256>" if dom == "update" else "k_apply_bf16<128,256>"
         result["roofline"] = {
-            "kernel": f"k_update_bf16<128,256>" if dom == "update" else "k_apply_bf16<128,256>",
+            "kernel": kname,
             "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": stored_traffic(dom, n_tok),
+            "traffic": None if wide else stored_traffic(dom, n_tok),
         }
         result["kernels"] = kern
     result["config"] = {
@@ -256,7 +268,11 @@ def main():
                      "f100": "100 frames x 1374 tokens + one 1374-token target view",
                      "f8": "8 frames x 1374 tokens",
                      "f700x24": "700-frame layer x 24 layers with fresh weights per layer",
-                     "stream256": "256 frames x 1374 tokens, one streaming step per frame"}[wl.name],
+                     "stream256": "256 frames x 1374 tokens, one streaming step per frame",
+                     "fw8": "8 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
+                     "fw100": "100 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
+                     "fw700": "700 frames x 1374 tokens, one full-width head (d 1024, hidden "
+                              "2048), one chunk"}[wl.name],
         "n_kv": wl.n_kv, "n_q": wl.n_q, "heads": wl.heads, "d_head": wl.d_head,
         "d_hidden": wl.d_hidden, "layers": wl.layers, "renorm": renorm,
         "io": "bf16 tokens, fp32 fast weights, fp32 accumulation",
@@ -265,7 +281,10 @@ def main():
     result["wall_s_timed"] = round(wall, 3)
 
     if not args.no_cpu_baseline:
-        ns = min(args.cpu_sample_tokens, wl.n_kv)
+        sample = args.cpu_sample_tokens
+        if sample <= 0:
+            sample = 131072 if wide else 262144
+        ns = min(sample, wl.n_kv)
         host = {k: x[k][:ns].to("cpu", torch.float64).numpy() for k in ("q", "k", "v", "eta")}
         for k in ("w1", "w2", "w3"):
             host[k] = x[k].cpu().double().numpy()

@@ -183,6 +183,11 @@ ZM_API int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks,
 /* Static description of a status code. */
 ZM_API const char* zm_status_string(int status);
 
+/* Description of the last ZM_ERR_HIP failure on the calling thread (the HIP
+ * call or GEMM-library call that failed and its status), or "" if none.
+ * The string stays valid until the thread's next failing call. */
+ZM_API const char* zm_ttt_last_error(void);
+
 /* Library version as major*10000 + minor*100 + patch. */
 ZM_API int zm_ttt_version(void);
 

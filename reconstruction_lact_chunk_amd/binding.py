@@ -22,8 +22,8 @@ STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
     "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-    "zm_ttt_stream_step", "zm_ttt_chunked", "zm_status_string", "zm_ttt_version",
-    "zm_ttt_set_profile_events",
+    "zm_ttt_stream_step", "zm_ttt_chunked", "zm_status_string", "zm_ttt_last_error",
+    "zm_ttt_version", "zm_ttt_set_profile_events",
 )
 
 
@@ -73,6 +73,8 @@ def load_library(path: str | None = None):
                                    _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.zm_status_string.argtypes = [ctypes.c_int]
     lib.zm_status_string.restype = ctypes.c_char_p
+    lib.zm_ttt_last_error.argtypes = []
+    lib.zm_ttt_last_error.restype = ctypes.c_char_p
     lib.zm_ttt_version.argtypes = []
     lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
     for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
@@ -92,9 +94,14 @@ def version() -> int:
     return int(load_library().zm_ttt_version())
 
 
+def last_error() -> str:
+    return load_library().zm_ttt_last_error().decode()
+
+
 def _check(status: int, what: str):
     if status != OK:
-        raise ZmError(f"{what}: {status_string(status)} ({status})", status)
+        detail = f"; {last_error()}" if status == ERR_HIP else ""
+        raise ZmError(f"{what}: {status_string(status)} ({status}){detail}", status)
 
 
 # ---------------------------------------------------------------------------

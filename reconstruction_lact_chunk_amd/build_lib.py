@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libzmttt.so")
 ARCH = "gfx950"
 
 SOURCES = ["weights.hip", "update_bf16.hip", "apply_bf16.hip", "fp32_path.hip",
-           "newton_schulz.hip", "api.cpp"]
+           "newton_schulz.hip", "wide_kernels.hip", "wide_path.cpp", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",
@@ -61,7 +61,10 @@ def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), SOURCES))
     tmp = out + ".tmp"
-    cmd = [hipcc(), *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs]
+    rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
+    # hipBLASLt serves the plain GEMMs of the full-width head shape
+    cmd = [hipcc(), *DEVICE, "-shared", "-fPIC", "-o", tmp, *objs, f"-L{rocm_lib}", "-lhipblaslt",
+           f"-Wl,-rpath,{rocm_lib}"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

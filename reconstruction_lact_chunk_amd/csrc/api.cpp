@@ -6,7 +6,24 @@
 
 #include <hip/hip_runtime.h>
 
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "wide_path.h"
 #include "zm_internal.h"
+
+namespace zm {
+
+thread_local char g_last_error[512] = "";
+
+void set_last_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+}
+
+}  // namespace zm
 
 using namespace zm;
 
@@ -52,26 +69,45 @@ int check_desc(const zm_ttt_desc* d) {
     return ZM_ERR_INVALID_ARG;
   if (d->ld_tok < (int64_t)d->heads * d->d_head || d->ld_tok % 8 != 0) return ZM_ERR_INVALID_ARG;
   if (d->heads > 64) return ZM_ERR_UNSUPPORTED;
+  if (wide_shape(d->d_head, d->d_hidden)) {
+    // full width: bf16 io and the plain gradient step only
+    if (d->io_dtype != ZM_BF16 || d->step_rule != ZM_STEP_GRADIENT) return ZM_ERR_UNSUPPORTED;
+    return ZM_OK;
+  }
   const bool ok_shape = (d->d_head == 64 || d->d_head == 128) &&
                         (d->d_hidden == 128 || d->d_hidden == 256);
   if (!ok_shape) return ZM_ERR_UNSUPPORTED;
   return ZM_OK;
 }
 
+inline bool is_wide(const zm_ttt_desc* d) { return wide_shape(d->d_head, d->d_hidden); }
+
+// Caller's workspace.
+struct Ws {
+  void* p;
+  size_t bytes;
+};
+
 struct Layout {
   size_t set_a, set_b, part, total;
   UpdatePlan plan;
 };
 
-// Workspace: two bf16 weight sets (4 arrays each) and the partial sums.
-Layout layout(const zm_ttt_desc* d, int64_t n_kv) {
+// Workspace: two bf16 weight sets (4 arrays each), then the partial sums (or,
+// for the full width, the token-block buffers and the partial sums).
+Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
   Layout L;
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const size_t set_bytes = round_up(4 * welems * sizeof(uint16_t), 256);
-  L.plan = plan_update(n_kv, d->heads, d->d_hidden);
   L.set_a = 0;
   L.set_b = set_bytes;
   L.part = 2 * set_bytes;
+  if (is_wide(d)) {
+    L.plan = UpdatePlan{(int)wide_splits(n_kv), kWideBlock};
+    L.total = L.part + wide_extra_bytes(d->heads, d->d_head, d->d_hidden, n_kv, n_q);
+    return L;
+  }
+  L.plan = plan_update(n_kv, d->heads, d->d_hidden);
   L.total = L.part + round_up((size_t)L.plan.splits * 3 * welems * sizeof(float), 256);
   return L;
 }
@@ -105,8 +141,8 @@ int check_weights(const float* a, const float* b, const float* c) {
   return ZM_OK;
 }
 
-int check_ws(const zm_ttt_desc* d, int64_t n_kv, void* ws, size_t ws_bytes) {
-  const Layout L = layout(d, n_kv);
+int check_ws(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q, void* ws, size_t ws_bytes) {
+  const Layout L = layout(d, n_kv, n_q);
   if (!ws) return ZM_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return ZM_ERR_INVALID_ARG;
   if (ws_bytes < L.total) return ZM_ERR_WORKSPACE;
@@ -119,9 +155,13 @@ int check_ws(const zm_ttt_desc* d, int64_t n_kv, void* ws, size_t ws_bytes) {
     if (_s != ZM_OK) return _s; \
   } while (0)
 
-#define ZM_HIP(expr)                          \
-  do {                                        \
-    if ((expr) != hipSuccess) return ZM_ERR_HIP; \
+#define ZM_HIP(expr)                                                                \
+  do {                                                                              \
+    const hipError_t _e = (expr);                                                   \
+    if (_e != hipSuccess) {                                                         \
+      zm::set_last_error("%s: %s (%d)", #expr, hipGetErrorString(_e), (int)_e);     \
+      return ZM_ERR_HIP;                                                            \
+    }                                                                               \
   } while (0)
 
 // The update part shared by update, update_apply and stream_step: partial
@@ -129,10 +169,27 @@ int check_ws(const zm_ttt_desc* d, int64_t n_kv, void* ws, size_t ws_bytes) {
 // emit is non-null the reduce also writes the bf16 copies of W_hat there.
 int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, const float* eta,
                const float* w1, const float* w2, const float* w3, float* o1, float* o2,
-               float* o3, void* ws, const WSet* emit, bool cast_done, hipStream_t st) {
-  const Layout L = layout(d, n);
+               float* o3, Ws wsp, const WSet* emit, bool cast_done, hipStream_t st) {
+  void* const ws = wsp.p;
+  const Layout L = layout(d, n, 0);
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const WSet a = carve_set(ws, L.set_a, welems);
+  if (is_wide(d)) {
+    const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n);
+    if (n > 0) {
+      if (!cast_done) {
+        Scoped s(kStageCast, st);
+        ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
+      }
+      Scoped s(kStageUpdate, st);
+      ZM_TRY(wide_update(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)k,
+                         (const uint16_t*)v, eta, a, wb, st));
+    }
+    Scoped s(kStageReduce, st);
+    ZM_HIP(launch_wide_reduce(wb.part, L.plan.splits, d->heads, d->d_head, d->d_hidden, w1, w2,
+                              w3, o1, o2, o3, d->renorm, emit, st));
+    return ZM_OK;
+  }
   float* part = (float*)((char*)ws + L.part);
   if (n > 0) {
     if (d->io_dtype == ZM_BF16) {
@@ -166,9 +223,15 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
 // Apply through fp32 weights w* (fp32 path) or through the bf16 set `set`
 // (bf16 path; the caller has filled it).
 int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const float* w1,
-              const float* w2, const float* w3, const WSet& set, hipStream_t st) {
+              const float* w2, const float* w3, const WSet& set, Ws wsp, hipStream_t st) {
   if (n == 0) return ZM_OK;
   Scoped s(kStageApply, st);
+  if (is_wide(d)) {
+    const Layout L = layout(d, 0, n);
+    const WideBufs wb = wide_bufs(wsp.p, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, 0);
+    return wide_apply(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)q,
+                      (uint16_t*)o, set, wb, st);
+  }
   if (d->io_dtype == ZM_BF16) {
     ZM_HIP(launch_apply_bf16((const uint16_t*)q, (uint16_t*)o, n, d->ld_tok, d->heads, d->d_head,
                              d->d_hidden, set, st));
@@ -185,11 +248,11 @@ int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const flo
 // first.  do_update = false only reads.  W is updated in place.
 int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_t n,
               const void* q, const void* k, const void* v, const float* eta, float* w1, float* w2,
-              float* w3, void* o, void* ws, hipStream_t st) {
+              float* w3, void* o, Ws ws, hipStream_t st) {
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
-  const Layout L = layout(d, n);
-  const WSet a = carve_set(ws, L.set_a, welems);
-  const WSet b = carve_set(ws, L.set_b, welems);
+  const Layout L = layout(d, n, n);
+  const WSet a = carve_set(ws.p, L.set_a, welems);
+  const WSet b = carve_set(ws.p, L.set_b, welems);
   const bool bf16 = d->io_dtype == ZM_BF16;
   const int updates = do_update ? inner : 0;
   if (order == ZM_APPLY_THEN_UPDATE || updates == 0) {
@@ -198,7 +261,7 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
       Scoped s(kStageCast, st);
       ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
     }
-    ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, st));
+    ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, ws, st));
     for (int i = 0; i < updates; ++i)
       ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws, nullptr, bf16 && i == 0, st));
     return ZM_OK;
@@ -207,7 +270,7 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
   for (int i = 0; i < updates; ++i)
     ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws,
                       (bf16 && n > 0 && i == updates - 1) ? &b : nullptr, false, st));
-  return run_apply(d, n, q, o, w1, w2, w3, b, st);
+  return run_apply(d, n, q, o, w1, w2, w3, b, ws, st);
 }
 
 inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2 : 4; }
@@ -217,6 +280,8 @@ inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2
 extern "C" {
 
 int zm_ttt_version(void) { return kVersion; }
+
+const char* zm_ttt_last_error(void) { return g_last_error; }
 
 const char* zm_status_string(int status) {
   switch (status) {
@@ -246,7 +311,7 @@ int zm_ttt_workspace_size(const zm_ttt_desc* desc, int64_t n_kv, int64_t n_q, si
   ZM_TRY(check_desc(desc));
   ZM_TRY(check_counts(n_kv, n_q));
   if (!bytes) return ZM_ERR_INVALID_ARG;
-  *bytes = layout(desc, n_kv).total;
+  *bytes = layout(desc, n_kv, n_q).total;
   return ZM_OK;
 }
 
@@ -261,10 +326,10 @@ int zm_ttt_update(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const vo
   ZM_TRY(check_eta(eta, n_kv));
   ZM_TRY(check_weights(w1, w2, w3));
   ZM_TRY(check_weights(w1_out, w2_out, w3_out));
-  ZM_TRY(check_ws(desc, n_kv, workspace, workspace_bytes));
+  ZM_TRY(check_ws(desc, n_kv, 0, workspace, workspace_bytes));
   hipStream_t st = (hipStream_t)stream;
-  return run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, workspace,
-                    nullptr, false, st);
+  return run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out,
+                    Ws{workspace, workspace_bytes}, nullptr, false, st);
 }
 
 int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q, const float* w1,
@@ -275,17 +340,17 @@ int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q, const floa
   ZM_TRY(check_tokens(q, n_q));
   ZM_TRY(check_tokens(o, n_q));
   ZM_TRY(check_weights(w1, w2, w3));
-  ZM_TRY(check_ws(desc, 0, workspace, workspace_bytes));
+  ZM_TRY(check_ws(desc, 0, n_q, workspace, workspace_bytes));
   if (n_q == 0) return ZM_OK;
   hipStream_t st = (hipStream_t)stream;
   const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
-  const Layout L = layout(desc, 0);
+  const Layout L = layout(desc, 0, n_q);
   const WSet a = carve_set(workspace, L.set_a, welems);
   if (desc->io_dtype == ZM_BF16) {
     Scoped s(kStageCast, st);
     ZM_HIP(launch_cast(w1, w2, w3, desc->heads, desc->d_head, desc->d_hidden, a, st));
   }
-  return run_apply(desc, n_q, q, o, w1, w2, w3, a, st);
+  return run_apply(desc, n_q, q, o, w1, w2, w3, a, Ws{workspace, workspace_bytes}, st);
 }
 
 int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const void* v,
@@ -302,15 +367,16 @@ int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv, const void* k, co
   ZM_TRY(check_tokens(o, n_q));
   ZM_TRY(check_weights(w1, w2, w3));
   ZM_TRY(check_weights(w1_out, w2_out, w3_out));
-  ZM_TRY(check_ws(desc, n_kv, workspace, workspace_bytes));
+  ZM_TRY(check_ws(desc, n_kv, n_q, workspace, workspace_bytes));
   hipStream_t st = (hipStream_t)stream;
   const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
-  const Layout L = layout(desc, n_kv);
+  const Layout L = layout(desc, n_kv, n_q);
   const WSet b = carve_set(workspace, L.set_b, welems);
   const bool bf16 = desc->io_dtype == ZM_BF16;
-  ZM_TRY(run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, workspace,
+  const Ws ws{workspace, workspace_bytes};
+  ZM_TRY(run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, ws,
                     (bf16 && n_q > 0) ? &b : nullptr, false, st));
-  return run_apply(desc, n_q, q, o, w1_out, w2_out, w3_out, b, st);
+  return run_apply(desc, n_q, q, o, w1_out, w2_out, w3_out, b, ws, st);
 }
 
 int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, const void* q,
@@ -326,9 +392,9 @@ int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, cons
   ZM_TRY(check_eta(eta, n_frame));
   ZM_TRY(check_tokens(o, n_frame));
   ZM_TRY(check_weights(w1, w2, w3));
-  ZM_TRY(check_ws(desc, n_frame, workspace, workspace_bytes));
-  return run_chunk(desc, order, true, 1, n_frame, q, k, v, eta, w1, w2, w3, o, workspace,
-                   (hipStream_t)stream);
+  ZM_TRY(check_ws(desc, n_frame, n_frame, workspace, workspace_bytes));
+  return run_chunk(desc, order, true, 1, n_frame, q, k, v, eta, w1, w2, w3, o,
+                   Ws{workspace, workspace_bytes}, (hipStream_t)stream);
 }
 
 int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const int64_t* offsets,
@@ -357,7 +423,7 @@ int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const i
   ZM_TRY(check_eta(eta, n));
   ZM_TRY(check_tokens(o, n));
   ZM_TRY(check_weights(w1, w2, w3));
-  ZM_TRY(check_ws(desc, longest, workspace, workspace_bytes));
+  ZM_TRY(check_ws(desc, longest, longest, workspace, workspace_bytes));
   hipStream_t st = (hipStream_t)stream;
   const size_t row = (size_t)desc->ld_tok * io_bytes(desc);  // bytes per token row
   for (int64_t c = 0; c < n_chunks; ++c) {
@@ -367,7 +433,7 @@ int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const i
     const bool upd = update_mask == nullptr || update_mask[c] != 0;
     ZM_TRY(run_chunk(desc, order, upd, inner_steps, len, (const char*)q + tok,
                      (const char*)k + tok, (const char*)v + tok, eta + s0 * desc->heads, w1, w2,
-                     w3, (char*)o + tok, workspace, st));
+                     w3, (char*)o + tok, Ws{workspace, workspace_bytes}, st));
   }
   return ZM_OK;
 }

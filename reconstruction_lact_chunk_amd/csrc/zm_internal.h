@@ -90,6 +90,10 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Records a description of the last failure on this thread (read back through
+// zm_ttt_last_error); printf-style.
+void set_last_error(const char* fmt, ...);
+
 // ---- split plan ------------------------------------------------------------
 struct UpdatePlan {
   int splits;        // S: token chunks (partial sums) per head

@@ -101,6 +101,27 @@ def test_step_rules_accepted_without_extra_workspace(rule):
     assert ws_size(desc(step_rule=rule), 10_992, 10_992) == ws_size(desc(), 10_992, 10_992)
 
 
+def test_full_width_shape_workspace_and_limits():
+    de = desc(heads=1, d=1024, h=2048)
+    st, base = ws_size(de, 0, 0)
+    assert st == 0
+    welems = 1024 * 2048
+    sets = 2 * 4 * welems * 2
+    gemm_ws = 64 << 20
+    assert base == sets + gemm_ws
+    blk = 65536
+    # token-block buffers (3 h bf16 per token, at most one block); 8 fp32
+    # partial slots of 3 h d (one for fewer than 8 tokens)
+    assert ws_size(de, 1000, 0)[1] == base + 1000 * 3 * 2048 * 2 + 8 * 3 * welems * 4
+    assert ws_size(de, 5, 0)[1] == base + 5 * 3 * 2048 * 2 + 3 * welems * 4
+    assert ws_size(de, 0, 1000)[1] == base + 1000 * 3 * 2048 * 2
+    assert ws_size(de, 200_000, 10)[1] == base + blk * 3 * 2048 * 2 + 8 * 3 * welems * 4
+    assert ws_size(desc(heads=1, d=1024, h=2048, io=zm.F32), 10, 10)[0] == zm.ERR_UNSUPPORTED
+    assert ws_size(desc(heads=1, d=1024, h=2048, step_rule=zm.STEP_NEWTON_SCHULZ), 10, 10)[0] \
+        == zm.ERR_UNSUPPORTED
+    assert ws_size(desc(heads=1, d=1024, h=1024), 10, 10)[0] == zm.ERR_UNSUPPORTED
+
+
 def test_null_descriptor_and_counts():
     out = ctypes.c_size_t(0)
     assert lib().zm_ttt_workspace_size(None, 1, 1, ctypes.byref(out)) == zm.ERR_INVALID_ARG

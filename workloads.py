@@ -87,8 +87,17 @@ WORKLOADS = {
                         description="the 700-frame layer repeated 24 times"),
     "stream256": Workload("stream256", 256, 518, 8, 128, 256, "bf16", True, streaming=True,
                           description="256 frames fed one at a time"),
+    # the full-width fast weight: one head of the whole model width 1024 with
+    # hidden 2048 (a 6 d^2 state, d = 1024)
+    "fw8": Workload("fw8", 8, 518, 1, 1024, 2048, "bf16", True,
+                    description="8 frames x 1374 tokens, one full-width head 1024 / 2048"),
+    "fw100": Workload("fw100", 100, 518, 1, 1024, 2048, "bf16", True,
+                      description="100 frames x 1374 tokens, one full-width head"),
+    "fw700": Workload("fw700", 700, 518, 1, 1024, 2048, "bf16", True,
+                      description="700 frames x 1374 tokens, one full-width head, one chunk"),
 }
-CONFIG_IDS = {"tiny": 1, "f8": 2, "f100": 3, "f700": 4, "f700x24": 4, "stream256": 5}
+CONFIG_IDS = {"tiny": 1, "f8": 2, "f100": 3, "f700": 4, "f700x24": 4, "stream256": 5,
+              "fw8": 6, "fw100": 7, "fw700": 8}
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_ETA, STREAM_QX = 1, 2, 3, 4, 5
 STREAM_W = 100  # + layer
