@@ -22,7 +22,11 @@
  * ---------------------------------------
  *  - Memory: every pointer is device memory owned by the caller.  The library
  *    allocates nothing, keeps no state between calls (apart from the optional
- *    profiling events below) and never synchronises the stream.
+ *    profiling events below) and never synchronises the stream.  Exception:
+ *    the full-width shape (d_head 1024, d_hidden 2048) runs its dense products
+ *    through hipBLASLt, whose handle the library creates on the first such
+ *    call on a device (the GEMM library then holds its own resources until the
+ *    process ends) and whose chosen algorithm per problem shape it caches.
  *  - Token tensors q, k, v, o: [n, heads, d_head] with a token stride of
  *    desc->ld_tok elements (ld_tok >= heads * d_head, multiple of 8).  Element
  *    type: bf16 or fp32 (desc->io_dtype).  Base pointers 16-byte aligned.
@@ -41,7 +45,10 @@
  *    caller's next synchronisation.  NaN/Inf inputs propagate (one NaN token
  *    poisons the chunk sum); they are not checked.
  *  - Supported shapes: (d_head, d_hidden) in {(64,128), (64,256), (128,128),
- *    (128,256)}; heads in [1, 64]; others return ZM_ERR_UNSUPPORTED.
+ *    (128,256)}, and the full-width (1024, 2048) with bf16 io and the plain
+ *    gradient step (the ZipMap notes' single full-width fast weight with a
+ *    6 d^2 state, d = 1024); heads in [1, 64]; others return
+ *    ZM_ERR_UNSUPPORTED.
  *  - Results are deterministic: the split of the token sum depends only on
  *    (n, heads, d_head, d_hidden), and partial sums are combined in a fixed
  *    order without atomics.
