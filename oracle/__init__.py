@@ -31,4 +31,9 @@ from .ttt_oracle import (  # noqa: F401
     chunked,
     virtual_loss,
     update_rows_sampled,
+    rmsnorm,
+    output_gate,
+    project,
+    layer,
+    RMS_EPS,
 )

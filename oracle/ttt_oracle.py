@@ -36,7 +36,14 @@ Readings taken where the pages leave a step open:
   * the optional renormalisation is per row (the fan-in vector of one output
     unit), with the pre-update row norm and a max(., 1e-12) guard;
   * bidirectional chunk: update first, then read with the updated weights;
-    streaming: apply-then-update per frame by default.
+    streaming: apply-then-update per frame by default;
+  * around the layer ([notes] q / k / v 投影; [review] the rate note under
+    Eq. (3) and Eq. (5)): q, k, v are linear projections of the input token;
+    the per-token rate comes from a linear layer, read as
+    eta = eta_scale * sigmoid(W_eta x) (positive and bounded; the pages name no
+    activation); the output gate is RMSNorm(o') * SiLU(W_g o') with RMSNorm
+    over the whole width (all heads), a learnable scale gamma and
+    eps = 1e-6 (the pages give neither), and it is the layer's output.
 """
 from __future__ import annotations
 
@@ -342,6 +349,48 @@ def chunked(q, k, v, eta, offsets, w1, w2, w3, order="update_then_apply", update
         if order == "update_then_apply":
             out[s:e] = apply(q[s:e], *w)
     return w, out
+
+
+# ---------------------------------------------------------------------------
+# Around the layer: input projections and the output gate
+# ---------------------------------------------------------------------------
+RMS_EPS = 1e-6
+
+
+def rmsnorm(x, gamma, eps=RMS_EPS):
+    """x / sqrt(mean(x^2) + eps) * gamma over the last axis ([review] Eq. (5))."""
+    x = _f64(x)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * _f64(gamma)
+
+
+def output_gate(o_prime, w_gate, gamma, eps=RMS_EPS):
+    """o = RMSNorm(o') * SiLU(W_g o') per token ([review] Eq. (5)).
+    o_prime: [n, width] (all heads side by side); w_gate: [width, width]."""
+    o_prime = _f64(o_prime)
+    return rmsnorm(o_prime, gamma, eps) * silu(o_prime @ _f64(w_gate).T)
+
+
+def project(x, w_in, heads, d, eta_scale):
+    """q, k, v = W_Q x, W_K x, W_V x ([notes] q / k / v 投影) and the rate
+    eta = eta_scale * sigmoid(W_eta x) ([review] note under Eq. (3)).
+    x: [n, d_in]; w_in: [3 H d + H, d_in] (rows W_Q, W_K, W_V, W_eta).
+    Returns q, k, v [n, H, d] and eta [n, H]."""
+    y = _f64(x) @ _f64(w_in).T
+    hd = heads * d
+    q, k, v = (y[:, i * hd:(i + 1) * hd].reshape(-1, heads, d) for i in range(3))
+    eta = eta_scale * sigmoid(y[:, 3 * hd:3 * hd + heads])
+    return q, k, v, eta
+
+
+def layer(x, w_in, w_gate, gamma, w1, w2, w3, eta_scale, renorm=False, eps=RMS_EPS,
+          step="gradient"):
+    """The whole TTT layer on one bidirectional chunk: projections, update on
+    every token, apply to every token, output gate.  Returns
+    ((W1_hat, W2_hat, W3_hat), o [n, H d])."""
+    heads, d = _f64(w1).shape[0], _f64(w1).shape[2]
+    q, k, v, eta = project(x, w_in, heads, d, eta_scale)
+    new, o_prime = update_apply(k, v, eta, q, w1, w2, w3, renorm=renorm, step=step)
+    return new, output_gate(o_prime.reshape(o_prime.shape[0], -1), w_gate, gamma, eps)
 
 
 def update_rows_sampled(k, v, eta, w1, w2, w3, hidden_idx, block=None):
