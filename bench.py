@@ -43,7 +43,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="f700",
-                   choices=["f700", "f100", "f8", "f700x24", "stream256", "fw8", "fw100", "fw700"])
+                   choices=["f700", "f100", "f8", "f700x24", "stream256", "fw8", "fw100", "fw700",
+                            "layer700"])
     p.add_argument("--seed", type=int, default=4)
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens for the oracle baseline (default: 262144 at the 8-head shape, "
@@ -105,6 +106,22 @@ def cpu_baseline(inputs_host, sample_tokens, renorm, step_rule="gradient"):
                       f"(n_q = n_kv = {sample_tokens}), NumPy fp64, {dt:.2f} s"}
 
 
+def cpu_baseline_layer(xs, w_in, w_gate, gamma, w, sample_tokens, renorm, step_rule):
+    """The fp64 oracle's whole layer on the first `sample_tokens` tokens."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.layer(xs, w_in, w_gate, gamma, *w, eta_scale=0.01, renorm=renorm, step=step_rule)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {sample_tokens} tokens of the workload through the whole layer "
+                      f"(projections, update + apply, output gate), NumPy fp64, {dt:.2f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -124,6 +141,7 @@ def main():
     torch.cuda.set_device(dev)
     wl = WL.WORKLOADS[args.workload]
     wide = wl.d_head == 1024
+    whole = wl.name.startswith("layer")
     renorm = not args.no_renorm and wl.renorm
     rule = zm.STEP_NEWTON_SCHULZ if args.step_rule == "newton_schulz" else zm.STEP_GRADIENT
     log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
@@ -154,6 +172,19 @@ def main():
     o = torch.empty_like(x["q"])
     w_out = [tuple(torch.empty_like(w) for w in wl_w) for wl_w in ws_layers]
     stream = torch.cuda.current_stream(dev)
+    if whole:
+        # the whole layer: tokens of the model width through the projections,
+        # the TTT update + apply and the output gate
+        lx, lw_in, lw_gate, lgamma = WL.make_layer_tensors(wl.n_kv, wl.heads, wl.d_head,
+                                                           args.seed, dev)
+        del x
+        x = {}
+        lo = torch.empty((wl.n_kv, wl.heads * wl.d_head), dtype=torch.bfloat16, device=dev)
+        ldesc = zm.Desc(wl.heads, wl.d_head, wl.d_hidden, zm.BF16,
+                        zm.RENORM_ROW if renorm else zm.RENORM_NONE, rule, wl.heads * wl.d_head)
+        lws = torch.empty(zm.layer_workspace_size(ldesc, zm.make_layer_weights(
+            lw_in, lw_gate, lgamma), wl.n_kv), dtype=torch.uint8, device=dev)
+        del ws
 
     def step(prof=None):
         if wl.streaming:
@@ -165,6 +196,10 @@ def main():
         for li, wl_w in enumerate(ws_layers):
             if prof is not None:
                 zm.set_profile_events(prof[li])
+            if whole:
+                zm.layer(lx, lw_in, lw_gate, lgamma, *wl_w, renorm=renorm, step_rule=rule,
+                         w_out=w_out[li], out=lo, workspace=lws)
+                continue
             zm.update_apply(x["k"], x["v"], x["eta"], x["q"], *wl_w, renorm=renorm,
                             w_out=w_out[li], out=o, workspace=ws, step_rule=rule)
         if prof is not None:
@@ -177,7 +212,7 @@ def main():
     K = args.steps
     prof = None
     if not wl.streaming:
-        prof = [[make_events(torch, 10) for _ in ws_layers] for _ in range(K)]
+        prof = [[make_events(torch, 14 if whole else 10) for _ in ws_layers] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
@@ -219,6 +254,9 @@ def main():
         names = {1: "update", 2: "reduce", 3: "apply", 0: "cast"}
         if rule == zm.STEP_NEWTON_SCHULZ:
             names[4] = "newton_schulz"
+        if whole:
+            names[5] = "project"
+            names[6] = "output_gate"
         durs = {nm: [] for nm in names.values()}
         for k in range(K):
             for li in range(len(ws_layers)):
@@ -239,6 +277,22 @@ def main():
                                     "accumulation) and the wide gate kernel")
         kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
         kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}
+        if whole:
+            width = wl.heads * wl.d_head
+            fl_proj = 2 * width * (3 * width + wl.heads) * n_tok
+            fl_gate = 2 * width * width * n_tok
+            kern["project"] = {"avg_ms": round(avg["project"], 4), "achieved_tflops": round(
+                fl_proj / (avg["project"] / 1e3) / 1e12, 1), "what": "hipBLASLt GEMM x W_in^T "
+                "(q, k, v and rate logits) + k_eta_from_logits"}
+            kern["output_gate"] = {"avg_ms": round(avg["output_gate"], 4), "achieved_tflops": round(
+                fl_gate / (avg["output_gate"] / 1e3) / 1e12, 1), "what": "hipBLASLt GEMM o' W_g^T "
+                "+ k_rmsnorm_gate"}
+            per_layer_ms = ms / wl.layers
+            result["layer_flops_per_token"] = (fl_proj + fl_gate) // n_tok + \
+                wl.flops_per_token_update() + wl.flops_per_token_apply()
+            result["layer_frac_bf16_peak"] = round(
+                (flops_upd + flops_app + fl_proj + fl_gate) / (per_layer_ms / 1e3) / 1e12
+                / PEAK_BF16_TFLOPS, 4)
         if "newton_schulz" in avg:
             # five quintic steps per matrix: 4 M^2 N + 2 M^3 flops each (M = d, N = h)
             m, nn = wl.d_head, wl.d_hidden
@@ -272,7 +326,10 @@ def main():
                      "fw8": "8 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
                      "fw100": "100 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
                      "fw700": "700 frames x 1374 tokens, one full-width head (d 1024, hidden "
-                              "2048), one chunk"}[wl.name],
+                              "2048), one chunk",
+                     "layer700": "700 frames x 1374 tokens of width 1024 through the whole layer: "
+                                 "projections, update + apply (8 heads 128 / 256), output gate"
+                     }[wl.name],
         "n_kv": wl.n_kv, "n_q": wl.n_q, "heads": wl.heads, "d_head": wl.d_head,
         "d_hidden": wl.d_hidden, "layers": wl.layers, "renorm": renorm,
         "io": "bf16 tokens, fp32 fast weights, fp32 accumulation",
@@ -285,6 +342,15 @@ def main():
         if sample <= 0:
             sample = 131072 if wide else 262144
         ns = min(sample, wl.n_kv)
+        if whole:
+            ns = min(ns, 131072)
+            f64 = lambda t: t.to("cpu", torch.float64).numpy()  # noqa: E731
+            log(f"cpu baseline: oracle layer on {ns} tokens")
+            result["cpu_baseline"] = cpu_baseline_layer(
+                f64(lx[:ns]), f64(lw_in), f64(lw_gate), f64(lgamma),
+                [f64(t) for t in ws_layers[0]], ns, renorm, args.step_rule)
+            print(json.dumps(result), flush=True)
+            return
         host = {k: x[k][:ns].to("cpu", torch.float64).numpy() for k in ("q", "k", "v", "eta")}
         for k in ("w1", "w2", "w3"):
             host[k] = x[k].cpu().double().numpy()

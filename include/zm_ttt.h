@@ -190,6 +190,43 @@ ZM_API int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks,
 /* Static description of a status code. */
 ZM_API const char* zm_status_string(int status);
 
+/* The slow weights around the layer: the projections of an input token x
+ * (width d_in) to q, k, v (ZipMap notes, q / k / v 投影) and to the per-token
+ * rate (review, note under Eq. (3): a linear layer of the token), and the
+ * output gate of review Eq. (5).  Readings where the pages are silent: the
+ * rate is eta = eta_scale * sigmoid(W_eta x); RMSNorm runs over the whole
+ * width H * d_head with a learnable scale gamma and epsilon rms_eps. */
+typedef struct zm_layer_weights {
+  const void* w_in;     /* bf16 [3 H d + H][d_in]: rows of W_Q, W_K, W_V (H d each,
+                           head-major, d_head consecutive rows per head), then W_eta (H) */
+  const void* w_gate;   /* bf16 [H d][H d]: W_g */
+  const float* gamma;   /* fp32 [H d]: RMSNorm scale, 16-byte aligned */
+  int32_t d_in;         /* input width, a multiple of 8 */
+  float eta_scale;      /* >= 0 */
+  float rms_eps;        /* > 0 */
+  int32_t reserved;     /* must be 0 */
+} zm_layer_weights;
+
+/* Bytes of workspace zm_ttt_layer needs for n tokens. */
+ZM_API int zm_ttt_layer_workspace_size(const zm_ttt_desc* desc, const zm_layer_weights* lw,
+                                int64_t n, size_t* bytes);
+
+/* The whole TTT layer on one bidirectional chunk of n tokens x (bf16 rows of
+ * stride ld_x, ld_x >= d_in, a multiple of 8):
+ *   [q | k | v | z] = W_in x,  eta = eta_scale * sigmoid(z),
+ *   W_hat = update(W; k, v, eta) (+ renorm, desc->step_rule),
+ *   o' = f_{W_hat}(q),  o = RMSNorm(o') * SiLU(W_g o')  (review Eq. (5)).
+ * desc: heads, d_head, d_hidden, renorm and step_rule as for the other entry
+ * points; io_dtype must be ZM_BF16; desc->ld_tok is the row stride of o
+ * (>= H d, a multiple of 8).  w1..w3 are read, W_hat goes to w*_out (may
+ * alias).  o: bf16 [n][H d].  The projections and W_g o' run as library GEMMs
+ * (bf16 operands, fp32 accumulation, bf16 results); the rate, the gate and the
+ * TTT steps run in the library's kernels. */
+ZM_API int zm_ttt_layer(const zm_ttt_desc* desc, const zm_layer_weights* lw, int64_t n,
+                 const void* x, int64_t ld_x, const float* w1, const float* w2, const float* w3,
+                 float* w1_out, float* w2_out, float* w3_out, void* o,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
 /* Description of the last ZM_ERR_HIP failure on the calling thread (the HIP
  * call or GEMM-library call that failed and its status), or "" if none.
  * The string stays valid until the thread's next failing call. */
@@ -200,9 +237,10 @@ ZM_API int zm_ttt_version(void);
 
 /* Profiling aid: when events != NULL, every later launch of kernel stage s
  * (0 weight cast, 1 update partial sums, 2 reduce/step/renorm, 3 apply,
- * 4 Newton-Schulz) records events[2s] before and events[2s+1] after itself on
- * the launch stream, for each non-NULL slot.  The events are hipEvent_t
- * handles passed as void*; n_events must be 8 (stages 0-3) or 10 (or 0 with
+ * 4 Newton-Schulz, 5 input projections and rate, 6 output gate) records
+ * events[2s] before and events[2s+1] after itself on the launch stream, for
+ * each non-NULL slot.  The events are hipEvent_t handles passed as void*;
+ * n_events must be 8 (stages 0-3), 10 (0-4) or 14 (0-6) (or 0 with
  * events == NULL to switch off).  Process-wide setting; not for concurrent use
  * from several threads. */
 ZM_API int zm_ttt_set_profile_events(void* const* events, int n_events);

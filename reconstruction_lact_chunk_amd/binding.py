@@ -22,8 +22,8 @@ STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
     "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-    "zm_ttt_stream_step", "zm_ttt_chunked", "zm_status_string", "zm_ttt_last_error",
-    "zm_ttt_version", "zm_ttt_set_profile_events",
+    "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size", "zm_ttt_layer",
+    "zm_status_string", "zm_ttt_last_error", "zm_ttt_version", "zm_ttt_set_profile_events",
 )
 
 
@@ -42,6 +42,18 @@ class Desc(ctypes.Structure):
         ("renorm", ctypes.c_int32),
         ("step_rule", ctypes.c_int32),
         ("ld_tok", ctypes.c_int64),
+    ]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [
+        ("w_in", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p),
+        ("gamma", ctypes.c_void_p),
+        ("d_in", ctypes.c_int32),
+        ("eta_scale", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -71,6 +83,10 @@ def load_library(path: str | None = None):
                                        _P, _SZ, _P]
     lib.zm_ttt_chunked.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, ctypes.c_int, _P, _P, _P,
                                    _P, _P, _P, _P, _P, _P, _SZ, _P]
+    _LW = ctypes.POINTER(LayerWeights)
+    lib.zm_ttt_layer_workspace_size.argtypes = [_DESC, _LW, _I64, ctypes.POINTER(_SZ)]
+    lib.zm_ttt_layer.argtypes = [_DESC, _LW, _I64, _P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                 _P]
     lib.zm_status_string.argtypes = [ctypes.c_int]
     lib.zm_status_string.restype = ctypes.c_char_p
     lib.zm_ttt_last_error.argtypes = []
@@ -78,8 +94,8 @@ def load_library(path: str | None = None):
     lib.zm_ttt_version.argtypes = []
     lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
     for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-                 "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_version",
-                 "zm_ttt_set_profile_events"):
+                 "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size",
+                 "zm_ttt_layer", "zm_ttt_version", "zm_ttt_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -308,16 +324,66 @@ def chunked(q, k, v, eta, offsets, w1, w2, w3, renorm=False, order=UPDATE_THEN_A
     return o
 
 
+def make_layer_weights(w_in, w_gate, gamma, eta_scale=0.01, rms_eps=1e-6) -> LayerWeights:
+    for t, nm in ((w_in, "w_in"), (w_gate, "w_gate")):
+        if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.dim() != 2 or not t.is_cuda:
+            raise ZmError(f"{nm} must be a contiguous 2-D bf16 GPU tensor")
+    if gamma.dtype != torch.float32 or not gamma.is_contiguous() or not gamma.is_cuda:
+        raise ZmError("gamma must be a contiguous fp32 GPU tensor")
+    return LayerWeights(w_in.data_ptr(), w_gate.data_ptr(), gamma.data_ptr(), w_in.shape[1],
+                        float(eta_scale), float(rms_eps), 0)
+
+
+def layer_workspace_size(desc: Desc, lw: LayerWeights, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().zm_ttt_layer_workspace_size(ctypes.byref(desc), ctypes.byref(lw), int(n),
+                                                       ctypes.byref(out)),
+           "zm_ttt_layer_workspace_size")
+    return int(out.value)
+
+
+def layer(x, w_in, w_gate, gamma, w1, w2, w3, eta_scale=0.01, rms_eps=1e-6, renorm=False,
+          step_rule=STEP_GRADIENT, w_out=None, out=None, workspace=None):
+    """The whole layer on one chunk: projections of x [n, d_in] (bf16) to q, k,
+    v and the rate, update, apply, output gate.  Returns ((W1_hat, W2_hat,
+    W3_hat), o [n, H d] bf16)."""
+    heads, d, h = _check_weights(w1, w2, w3)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or (x.shape[0] > 1 and
+                                                                       x.stride(1) != 1):
+        raise ZmError("x must be a 2-D bf16 GPU tensor with unit column stride")
+    n = x.shape[0]
+    if tuple(w_in.shape) != (3 * heads * d + heads, x.shape[1]):
+        raise ZmError(f"w_in must be [{3 * heads * d + heads}, {x.shape[1]}]")
+    if tuple(w_gate.shape) != (heads * d, heads * d) or tuple(gamma.shape) != (heads * d,):
+        raise ZmError("w_gate must be [H d, H d] and gamma [H d]")
+    o = out if out is not None else torch.empty((n, heads * d), dtype=torch.bfloat16,
+                                                device=x.device)
+    desc = Desc(heads, d, h, BF16, RENORM_ROW if renorm else RENORM_NONE, int(step_rule),
+                o.stride(0) if n > 1 else heads * d)
+    lw = make_layer_weights(w_in, w_gate, gamma, eta_scale, rms_eps)
+    need = layer_workspace_size(desc, lw, n)
+    ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
+                                                             device=x.device)
+    outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_weights(*outs)
+    st = load_library().zm_ttt_layer(
+        ctypes.byref(desc), ctypes.byref(lw), n, _ptr(x), x.stride(0) if n > 1 else x.shape[1],
+        _ptr(w1), _ptr(w2), _ptr(w3), *map(_ptr, outs), _ptr(o), _ptr(ws), _ws_bytes(ws),
+        _stream(x.device))
+    _check(st, "zm_ttt_layer")
+    return outs, o
+
+
 def set_profile_events(events):
-    """events: 8 or 10 torch.cuda.Event (or None entries) recorded around the
-    kernel stages (cast, update partials, reduce, apply, Newton-Schulz); None
-    switches off."""
+    """events: 8, 10 or 14 torch.cuda.Event (or None entries) recorded around
+    the kernel stages (cast, update partials, reduce, apply, Newton-Schulz,
+    projections, output gate); None switches off."""
     lib = load_library()
     if events is None:
         _check(lib.zm_ttt_set_profile_events(None, 0), "zm_ttt_set_profile_events")
         return
-    if len(events) not in (8, 10):
-        raise ZmError("need 8 or 10 event slots")
+    if len(events) not in (8, 10, 14):
+        raise ZmError("need 8, 10 or 14 event slots")
     arr = (ctypes.c_void_p * len(events))()
     for i, e in enumerate(events):
         arr[i] = None if e is None else ctypes.c_void_p(int(e.cuda_event))

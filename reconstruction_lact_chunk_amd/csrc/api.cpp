@@ -9,6 +9,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include "gemm_lt.h"
+#include "layer_kernels.h"
 #include "wide_path.h"
 #include "zm_internal.h"
 
@@ -33,7 +35,7 @@ constexpr int kVersion = 10100;  // 1.1.0
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
-constexpr int kMaxProfEvents = 10;
+constexpr int kMaxProfEvents = 14;
 void* g_prof[kMaxProfEvents] = {};
 bool g_prof_on = false;
 
@@ -42,7 +44,9 @@ enum Stage {
   kStageUpdate = 1,
   kStageReduce = 2,
   kStageApply = 3,
-  kStageNewtonSchulz = 4
+  kStageNewtonSchulz = 4,
+  kStageProject = 5,
+  kStageOutputGate = 6
 };
 
 inline void prof_mark(int slot, hipStream_t st) {
@@ -275,6 +279,42 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
 
 inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2 : 4; }
 
+// Workspace of zm_ttt_layer: the projection rows Y [n][ldy] bf16 (q | k | v |
+// rate logits; later o' in the k columns and W_g o' in the v columns), eta,
+// the GEMM library workspace, then the TTT workspace (last, so the full-width
+// path's partial sums at its end stay inside it).
+struct LayerLayout {
+  int64_t width, ncols, ldy;
+  size_t off_eta, off_lt, off_ttt, total;
+  zm_ttt_desc tdesc;  // the TTT call's descriptor: q / k / v rows of stride ldy
+};
+
+LayerLayout layer_layout(const zm_ttt_desc* d, int64_t n) {
+  LayerLayout L;
+  L.width = (int64_t)d->heads * d->d_head;
+  L.ncols = 3 * L.width + d->heads;
+  L.ldy = (L.ncols + 7) / 8 * 8;
+  L.off_eta = round_up((size_t)n * L.ldy * sizeof(uint16_t), 256);
+  L.off_lt = L.off_eta + round_up((size_t)n * d->heads * sizeof(float), 256);
+  L.off_ttt = L.off_lt + kLtWorkspace;
+  L.tdesc = *d;
+  L.tdesc.ld_tok = L.ldy;
+  L.total = L.off_ttt + layout(&L.tdesc, n, n).total;
+  return L;
+}
+
+int check_layer_args(const zm_ttt_desc* d, const zm_layer_weights* lw, int64_t n) {
+  ZM_TRY(check_desc(d));
+  if (d->io_dtype != ZM_BF16) return ZM_ERR_UNSUPPORTED;
+  if (!lw || lw->reserved != 0) return ZM_ERR_INVALID_ARG;
+  if (lw->d_in < 8 || lw->d_in % 8 != 0 || lw->d_in > (1 << 20)) return ZM_ERR_INVALID_ARG;
+  if (!(lw->eta_scale >= 0.f) || !(lw->rms_eps > 0.f)) return ZM_ERR_INVALID_ARG;
+  if (!lw->w_in || !lw->w_gate || !lw->gamma) return ZM_ERR_INVALID_ARG;
+  if (!aligned(lw->w_in, 16) || !aligned(lw->w_gate, 16) || !aligned(lw->gamma, 16))
+    return ZM_ERR_INVALID_ARG;
+  return check_counts(n, n);
+}
+
 }  // namespace
 
 extern "C" {
@@ -301,7 +341,7 @@ int zm_ttt_set_profile_events(void* const* events, int n_events) {
     g_prof_on = false;
     return ZM_OK;
   }
-  if (n_events != 8 && n_events != kMaxProfEvents) return ZM_ERR_INVALID_ARG;
+  if (n_events != 8 && n_events != 10 && n_events != kMaxProfEvents) return ZM_ERR_INVALID_ARG;
   for (int i = 0; i < kMaxProfEvents; ++i) g_prof[i] = i < n_events ? events[i] : nullptr;
   g_prof_on = true;
   return ZM_OK;
@@ -395,6 +435,59 @@ int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, cons
   ZM_TRY(check_ws(desc, n_frame, n_frame, workspace, workspace_bytes));
   return run_chunk(desc, order, true, 1, n_frame, q, k, v, eta, w1, w2, w3, o,
                    Ws{workspace, workspace_bytes}, (hipStream_t)stream);
+}
+
+int zm_ttt_layer_workspace_size(const zm_ttt_desc* desc, const zm_layer_weights* lw, int64_t n,
+                                size_t* bytes) {
+  ZM_TRY(check_layer_args(desc, lw, n));
+  if (!bytes) return ZM_ERR_INVALID_ARG;
+  *bytes = layer_layout(desc, n).total;
+  return ZM_OK;
+}
+
+int zm_ttt_layer(const zm_ttt_desc* desc, const zm_layer_weights* lw, int64_t n, const void* x,
+                 int64_t ld_x, const float* w1, const float* w2, const float* w3, float* w1_out,
+                 float* w2_out, float* w3_out, void* o, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  ZM_TRY(check_layer_args(desc, lw, n));
+  if (ld_x < lw->d_in || ld_x % 8 != 0) return ZM_ERR_INVALID_ARG;
+  ZM_TRY(check_tokens(x, n));
+  ZM_TRY(check_tokens(o, n));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_weights(w1_out, w2_out, w3_out));
+  const LayerLayout LL = layer_layout(desc, n);
+  if (desc->ld_tok < LL.width) return ZM_ERR_INVALID_ARG;
+  if (!workspace) return ZM_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return ZM_ERR_INVALID_ARG;
+  if (workspace_bytes < LL.total) return ZM_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  uint16_t* y = (uint16_t*)ws;
+  float* eta = (float*)(ws + LL.off_eta);
+  const LtWs lt{ws + LL.off_lt, kLtWorkspace};
+  const Ws tws{ws + LL.off_ttt, workspace_bytes - LL.off_ttt};
+  const zm_ttt_desc* td = &LL.tdesc;
+  const int64_t W = LL.width;
+  if (n > 0) {
+    Scoped s(kStageProject, st);
+    if (!lt_rm_nt(n, LL.ncols, lw->d_in, x, ld_x, lw->w_in, lw->d_in, y, LL.ldy, false, lt, st))
+      return ZM_ERR_HIP;
+    ZM_HIP(launch_eta_from_logits(y, LL.ldy, 3 * W, desc->heads, lw->eta_scale, eta, n, st));
+  }
+  // update on k, v (columns W .. 3W), then o' = f_W_hat(q) into the k columns
+  const size_t welems = (size_t)desc->heads * desc->d_hidden * desc->d_head;
+  const WSet b = carve_set(tws.p, layout(td, n, n).set_b, welems);
+  ZM_TRY(run_update(td, n, y + W, y + 2 * W, eta, w1, w2, w3, w1_out, w2_out, w3_out, tws,
+                    n > 0 ? &b : nullptr, false, st));
+  if (n == 0) return ZM_OK;
+  ZM_TRY(run_apply(td, n, y, y + W, w1_out, w2_out, w3_out, b, tws, st));
+  // g = W_g o' into the v columns, then o = RMSNorm(o') * SiLU(g)
+  Scoped s(kStageOutputGate, st);
+  if (!lt_rm_nt(n, W, W, y + W, LL.ldy, lw->w_gate, W, y + 2 * W, LL.ldy, false, lt, st))
+    return ZM_ERR_HIP;
+  ZM_HIP(launch_rmsnorm_gate(y + W, LL.ldy, y + 2 * W, LL.ldy, lw->gamma, lw->rms_eps,
+                             (uint16_t*)o, desc->ld_tok, (int)W, n, st));
+  return ZM_OK;
 }
 
 int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const int64_t* offsets,

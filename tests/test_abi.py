@@ -214,6 +214,47 @@ def test_chunked_rejects_bad_schedules_before_any_hip_call():
     assert call_chunked(de, [0, 0, 0], q=None, eta=None, ws_bytes=ws_size(de, 0, 0)[1]) == zm.OK
 
 
+def lw_struct(d_in=1024, eta_scale=0.01, eps=1e-6, reserved=0, w_in=GOOD, gamma=GOOD):
+    return zm.LayerWeights(w_in.value if w_in is not None else None, GOOD.value,
+                           gamma.value if gamma is not None else None, d_in, eta_scale, eps,
+                           reserved)
+
+
+def layer_ws(de, lw, n):
+    out = ctypes.c_size_t(0)
+    st = lib().zm_ttt_layer_workspace_size(ctypes.byref(de), ctypes.byref(lw), n,
+                                           ctypes.byref(out))
+    return st, out.value
+
+
+def test_layer_workspace_and_argument_checks():
+    de = desc()
+    lw = lw_struct()
+    st, need = layer_ws(de, lw, 1000)
+    assert st == zm.OK
+    # projection rows (3 H d + H rounded to 8 bf16), eta, the GEMM workspace, the TTT workspace
+    ttt = ws_size(desc(ld=3080), 1000, 1000)[1]
+    rows = (1000 * 3080 * 2 + 255) // 256 * 256
+    eta = (1000 * 8 * 4 + 255) // 256 * 256
+    assert need == rows + eta + (64 << 20) + ttt
+    assert layer_ws(desc(io=zm.F32), lw, 10)[0] == zm.ERR_UNSUPPORTED
+    for bad in (lw_struct(d_in=12), lw_struct(d_in=0), lw_struct(eta_scale=-1.0),
+                lw_struct(eps=0.0), lw_struct(reserved=1), lw_struct(w_in=None),
+                lw_struct(gamma=P((1 << 20) + 4))):
+        assert layer_ws(de, bad, 10)[0] == zm.ERR_INVALID_ARG
+    L = lib()
+
+    def call(n=1000, x=GOOD, ld_x=1024, o=GOOD, ws_bytes=need, de=de):
+        return L.zm_ttt_layer(ctypes.byref(de), ctypes.byref(lw), n, x, ld_x, GOOD, GOOD, GOOD,
+                              GOOD, GOOD, GOOD, o, GOOD, ws_bytes, None)
+    assert call(x=None) == zm.ERR_INVALID_ARG
+    assert call(ld_x=1000) == zm.ERR_INVALID_ARG         # < d_in
+    assert call(ld_x=1028) == zm.ERR_INVALID_ARG         # not a multiple of 8
+    assert call(o=ODD) == zm.ERR_INVALID_ARG
+    assert call(ws_bytes=need - 1) == zm.ERR_WORKSPACE
+    assert call(de=desc(ld=1016)) == zm.ERR_INVALID_ARG   # o rows narrower than H d
+
+
 def test_profile_event_argument_checks():
     L = lib()
     assert L.zm_ttt_set_profile_events(None, 3) == zm.ERR_INVALID_ARG
@@ -222,6 +263,9 @@ def test_profile_event_argument_checks():
     assert L.zm_ttt_set_profile_events(arr, 9) == zm.ERR_INVALID_ARG
     assert L.zm_ttt_set_profile_events(arr, 8) == zm.OK
     assert L.zm_ttt_set_profile_events(arr, 10) == zm.OK
+    arr14 = (ctypes.c_void_p * 14)()
+    assert L.zm_ttt_set_profile_events(arr14, 14) == zm.OK
+    assert L.zm_ttt_set_profile_events(arr14, 12) == zm.ERR_INVALID_ARG
     assert L.zm_ttt_set_profile_events(None, 0) == zm.OK
 
 

@@ -95,9 +95,13 @@ WORKLOADS = {
                       description="100 frames x 1374 tokens, one full-width head"),
     "fw700": Workload("fw700", 700, 518, 1, 1024, 2048, "bf16", True,
                       description="700 frames x 1374 tokens, one full-width head, one chunk"),
+    # the whole layer around the TTT step: projections from 1024-wide tokens,
+    # update + apply, output gate
+    "layer700": Workload("layer700", 700, 518, 8, 128, 256, "bf16", True,
+                         description="700 frames x 1374 tokens through the whole layer"),
 }
 CONFIG_IDS = {"tiny": 1, "f8": 2, "f100": 3, "f700": 4, "f700x24": 4, "stream256": 5,
-              "fw8": 6, "fw100": 7, "fw700": 8}
+              "fw8": 6, "fw100": 7, "fw700": 8, "layer700": 9}
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_ETA, STREAM_QX = 1, 2, 3, 4, 5
 STREAM_W = 100  # + layer
@@ -141,6 +145,31 @@ def make_weights(heads: int, d_head: int, d_hidden: int, seed: int, device="cpu"
     w2 = _normal((heads, d_head, d_hidden), 1.0 / math.sqrt(d_hidden), device, seed, base + 1, torch.float32)
     w3 = _normal((heads, d_hidden, d_head), 1.0 / math.sqrt(d_head), device, seed, base + 2, torch.float32)
     return w1, w2, w3
+
+
+STREAM_X, STREAM_WIN, STREAM_WETA, STREAM_WG, STREAM_GAMMA = 6, 7, 8, 9, 10
+
+
+def make_layer_tensors(n: int, heads: int, d_head: int, seed: int, device="cpu",
+                       d_in: int | None = None):
+    """Input tokens and slow weights of the whole layer (synthetic stand-ins for
+    trained projections).  Scales follow the token recipe above: with
+    x ~ N(0, 1) (bf16), W_Q, W_K, W_V rows ~ N(0, 1 / (d_in d_head)) give q, k, v
+    of variance 1 / d_head; W_eta rows ~ N(0, 1 / d_in) give rate logits of
+    variance 1 (so eta = 0.01 sigmoid(.) as above); W_g ~ N(0, 1 / (H d_head));
+    gamma = 1 + 0.1 N(0, 1).  Returns x [n, d_in], w_in [3 H d + H, d_in] and
+    w_gate [H d, H d] in bf16, gamma [H d] fp32."""
+    width = heads * d_head
+    d_in = width if d_in is None else d_in
+    x = _normal((n, d_in), 1.0, device, seed, STREAM_X, torch.bfloat16)
+    w_qkv = _normal((3 * width, d_in), 1.0 / math.sqrt(d_in * d_head), device, seed, STREAM_WIN,
+                    torch.float32)
+    w_eta = _normal((heads, d_in), 1.0 / math.sqrt(d_in), device, seed, STREAM_WETA, torch.float32)
+    w_in = torch.cat([w_qkv, w_eta]).to(torch.bfloat16)
+    w_gate = _normal((width, width), 1.0 / math.sqrt(width), device, seed, STREAM_WG,
+                     torch.bfloat16)
+    gamma = 1.0 + _normal((width,), 0.1, device, seed, STREAM_GAMMA, torch.float32)
+    return x, w_in, w_gate, gamma
 
 
 def make_inputs(wl: Workload, seed: int | None = None, device="cpu", eta_scale: float = 1.0,
