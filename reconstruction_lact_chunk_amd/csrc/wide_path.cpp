@@ -33,6 +33,19 @@ bool rm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const vo
                   count, sa, sb, sc, beta);
 }
 
+// [x | b] rows of the token-block buffer: x = tokens (-log2(e) W1)^T and
+// b = tokens W3^T, [len][2 h].  With one head the bf16 W1 and W3 copies are
+// adjacent in the workspace, i.e. [W1; W3] is one [2 h][d] operand and the
+// two products are one GEMM.
+bool forward_w13(int64_t len, int h, int d, const uint16_t* tok, int64_t ld, const WSet& wb,
+                 int hd, int heads, uint16_t* ab, const WideBufs& w, hipStream_t st) {
+  const int64_t hd_elems = (int64_t)h * d;
+  if (heads == 1 && wb.w3b == wb.w1b + hd_elems)
+    return rm_nt(len, 2 * h, d, tok, ld, wb.w1b, d, ab, 2 * h, false, w, st);
+  return rm_nt(len, h, d, tok, ld, wb.w1b + hd * hd_elems, d, ab, 2 * h, false, w, st) &&
+         rm_nt(len, h, d, tok, ld, wb.w3b + hd * hd_elems, d, ab + h, 2 * h, false, w, st);
+}
+
 }  // namespace
 
 bool wide_shape(int d, int h) { return d == kWideD && h == kWideH; }
@@ -81,8 +94,7 @@ int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* 
       const uint16_t* vb = v + s0 * ld + (int64_t)hd * d;
       float* slot = w.part + (int64_t)hd * 3 * hd_elems;
       // forward on the keys: x = -log2(e) W1 k, b = W3 k, e = W2^T v
-      if (!rm_nt(len, h, d, kb, ld, wb.w1b + hd * hd_elems, d, ab, 2 * h, false, w, st) ||
-          !rm_nt(len, h, d, kb, ld, wb.w3b + hd * hd_elems, d, ab + h, 2 * h, false, w, st) ||
+      if (!forward_w13(len, h, d, kb, ld, wb, hd, heads, ab, w, st) ||
           !rm_nt(len, h, d, vb, ld, wb.w2tb + hd * hd_elems, d, e, h, false, w, st))
         return ZM_ERR_HIP;
       const hipError_t ge = launch_wide_gate_update(ab, e, eta + s0 * heads + hd, heads, len, h, st);
@@ -126,9 +138,7 @@ int wide_apply(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* q
       const int64_t len = (n - s0) < kWideBlock ? (n - s0) : kWideBlock;
       const uint16_t* qb = q + s0 * ld + (int64_t)hd * d;
       uint16_t* ob = o + s0 * ld + (int64_t)hd * d;
-      if (!rm_nt(len, h, d, qb, ld, wb.w1b + hd * hd_elems, d, w.ab, 2 * h, false, w, st) ||
-          !rm_nt(len, h, d, qb, ld, wb.w3b + hd * hd_elems, d, w.ab + h, 2 * h, false, w, st))
-        return ZM_ERR_HIP;
+      if (!forward_w13(len, h, d, qb, ld, wb, hd, heads, w.ab, w, st)) return ZM_ERR_HIP;
       const hipError_t ge = launch_wide_gate_apply(w.ab, len, h, st);
       if (ge != hipSuccess) {
         set_last_error("wide gate (apply) launch: %s", hipGetErrorString(ge));
