@@ -300,7 +300,9 @@ def main():
             kern["newton_schulz"] = {
                 "avg_ms": round(avg["newton_schulz"], 4),
                 "achieved_tflops": round(ns_flops / (avg["newton_schulz"] / 1e3) / 1e12, 2),
-                "workgroups": 3 * wl.heads}
+                "what": ("batched split-bf16 hipBLASLt GEMMs (3 per product) and elementwise "
+                         "kernels" if wide else
+                         f"one workgroup per matrix ({3 * wl.heads}), split-bf16 MFMA")}
         dom = max(("update", "apply"), key=lambda nm: avg[nm])
         fl_dom = units[dom][0]
         ach = fl_dom / (avg[dom] / 1e3) / 1e12

@@ -45,10 +45,9 @@
  *    caller's next synchronisation.  NaN/Inf inputs propagate (one NaN token
  *    poisons the chunk sum); they are not checked.
  *  - Supported shapes: (d_head, d_hidden) in {(64,128), (64,256), (128,128),
- *    (128,256)}, and the full-width (1024, 2048) with bf16 io and the plain
- *    gradient step (the ZipMap notes' single full-width fast weight with a
- *    6 d^2 state, d = 1024); heads in [1, 64]; others return
- *    ZM_ERR_UNSUPPORTED.
+ *    (128,256)}, and the full-width (1024, 2048) with bf16 io (the ZipMap
+ *    notes' single full-width fast weight with a 6 d^2 state, d = 1024);
+ *    heads in [1, 64]; others return ZM_ERR_UNSUPPORTED.
  *  - Results are deterministic: the split of the token sum depends only on
  *    (n, heads, d_head, d_hidden), and partial sums are combined in a fixed
  *    order without atomics.
@@ -100,7 +99,8 @@ typedef enum zm_order { ZM_APPLY_THEN_UPDATE = 0, ZM_UPDATE_THEN_APPLY = 1 } zm_
  *     (a, b, c) = (3.4445, -4.7750, 2.0315) from X = g / max(||g||_F, 1e-12),
  *     per head and per matrix.  Its products run in split-bf16 (hi + lo
  *     parts, three bf16 matrix-core products each, fp32 accumulation) with bf16
- *     io and in fp32 with fp32 io.  The result no longer scales with eta: the
+ *     io and in fp32 with fp32 io (at the full-width shape as batched library
+ *     GEMMs, three per product).  The result no longer scales with eta: the
  *     step has singular values near 1 whatever the gradient's size, so it is
  *     meant to be used with ZM_RENORM_ROW.  n_kv = 0 leaves W unchanged. */
 typedef enum zm_step_rule { ZM_STEP_GRADIENT = 0, ZM_STEP_NEWTON_SCHULZ = 1 } zm_step_rule;

@@ -22,7 +22,7 @@ ARCH = "gfx950"
 
 SOURCES = ["weights.hip", "update_bf16.hip", "apply_bf16.hip", "fp32_path.hip",
            "newton_schulz.hip", "wide_kernels.hip", "wide_path.cpp", "gemm_lt.cpp",
-           "layer_kernels.hip", "api.cpp"]
+           "layer_kernels.hip", "wide_ns.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",

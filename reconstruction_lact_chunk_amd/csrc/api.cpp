@@ -74,8 +74,8 @@ int check_desc(const zm_ttt_desc* d) {
   if (d->ld_tok < (int64_t)d->heads * d->d_head || d->ld_tok % 8 != 0) return ZM_ERR_INVALID_ARG;
   if (d->heads > 64) return ZM_ERR_UNSUPPORTED;
   if (wide_shape(d->d_head, d->d_hidden)) {
-    // full width: bf16 io and the plain gradient step only
-    if (d->io_dtype != ZM_BF16 || d->step_rule != ZM_STEP_GRADIENT) return ZM_ERR_UNSUPPORTED;
+    // full width: bf16 io only
+    if (d->io_dtype != ZM_BF16) return ZM_ERR_UNSUPPORTED;
     return ZM_OK;
   }
   const bool ok_shape = (d->d_head == 64 || d->d_head == 128) &&
@@ -108,7 +108,8 @@ Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
   L.part = 2 * set_bytes;
   if (is_wide(d)) {
     L.plan = UpdatePlan{(int)wide_splits(n_kv), kWideBlock};
-    L.total = L.part + wide_extra_bytes(d->heads, d->d_head, d->d_hidden, n_kv, n_q);
+    L.total = L.part + wide_extra_bytes(d->heads, d->d_head, d->d_hidden, n_kv, n_q,
+                                        d->step_rule == ZM_STEP_NEWTON_SCHULZ);
     return L;
   }
   L.plan = plan_update(n_kv, d->heads, d->d_hidden);
@@ -179,7 +180,9 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const WSet a = carve_set(ws, L.set_a, welems);
   if (is_wide(d)) {
-    const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n);
+    const bool ns = d->step_rule == ZM_STEP_NEWTON_SCHULZ;
+    const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n, ns);
+    int splits = L.plan.splits;
     if (n > 0) {
       if (!cast_done) {
         Scoped s(kStageCast, st);
@@ -189,9 +192,16 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
       ZM_TRY(wide_update(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)k,
                          (const uint16_t*)v, eta, a, wb, st));
     }
+    if (n > 0 && ns) {
+      Scoped s(kStageNewtonSchulz, st);
+      ZM_HIP(launch_sum_splits(wb.part, splits, d->heads, d->d_head, d->d_hidden, st));
+      ZM_TRY(wide_newton_schulz(wb.part, d->heads, d->d_head, d->d_hidden, wb.ns, wb.lt_ws,
+                                wb.lt_ws_bytes, st));
+      splits = 1;
+    }
     Scoped s(kStageReduce, st);
-    ZM_HIP(launch_wide_reduce(wb.part, L.plan.splits, d->heads, d->d_head, d->d_hidden, w1, w2,
-                              w3, o1, o2, o3, d->renorm, emit, st));
+    ZM_HIP(launch_wide_reduce(wb.part, splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1,
+                              o2, o3, d->renorm, emit, st));
     return ZM_OK;
   }
   float* part = (float*)((char*)ws + L.part);
@@ -232,7 +242,8 @@ int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const flo
   Scoped s(kStageApply, st);
   if (is_wide(d)) {
     const Layout L = layout(d, 0, n);
-    const WideBufs wb = wide_bufs(wsp.p, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, 0);
+    const WideBufs wb = wide_bufs(wsp.p, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, 0,
+                                  d->step_rule == ZM_STEP_NEWTON_SCHULZ);
     return wide_apply(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)q,
                       (uint16_t*)o, set, wb, st);
   }

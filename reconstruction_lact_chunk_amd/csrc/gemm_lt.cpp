@@ -144,9 +144,16 @@ bool gemm(hipblasOperation_t ta, hipblasOperation_t tb, int64_t m, int64_t n, in
 }  // namespace
 
 bool lt_rm_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-              int64_t ldb, void* C, int64_t ldc, bool out_f32, LtWs ws, hipStream_t st) {
+              int64_t ldb, void* C, int64_t ldc, bool out_f32, LtWs ws, hipStream_t st, int count,
+              int64_t sa, int64_t sb, int64_t sc, float beta) {
+  Batch bt;
+  bt.count = count;
+  bt.sa = sb;  // the column-major call swaps the operands
+  bt.sb = sa;
+  bt.sd = sc;
+  bt.beta = beta;
   return gemm(HIPBLAS_OP_T, HIPBLAS_OP_N, N, M, K, B, ldb, A, lda, C, ldc, out_f32, ws.p,
-              ws.bytes, st);
+              ws.bytes, st, bt);
 }
 
 bool lt_rm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,

@@ -358,15 +358,18 @@ hipError_t launch_ns_shape(float* part, int heads, bool f32, hipStream_t st) {
   return hipGetLastError();
 }
 
+hipError_t launch_sum_splits(float* part, int splits, int heads, int d, int h, hipStream_t st) {
+  const int64_t slot = (int64_t)heads * 3 * h * d;
+  if (splits <= 1) return hipSuccess;
+  const unsigned blocks = (unsigned)ceil_div(slot / 4, 256);
+  hipLaunchKernelGGL(k_sum_splits, dim3(blocks), dim3(256), 0, st, part, splits, slot);
+  return hipGetLastError();
+}
+
 hipError_t launch_newton_schulz(float* part, int splits, int heads, int d, int h, bool f32,
                                 hipStream_t st) {
-  const int64_t slot = (int64_t)heads * 3 * h * d;
-  if (splits > 1) {
-    const unsigned blocks = (unsigned)ceil_div(slot / 4, 256);
-    hipLaunchKernelGGL(k_sum_splits, dim3(blocks), dim3(256), 0, st, part, splits, slot);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  const hipError_t e = launch_sum_splits(part, splits, heads, d, h, st);
+  if (e != hipSuccess) return e;
   if (d == 64 && h == 128) return launch_ns_shape<64, 128>(part, heads, f32, st);
   if (d == 64 && h == 256) return launch_ns_shape<64, 256>(part, heads, f32, st);
   if (d == 128 && h == 128) return launch_ns_shape<128, 128>(part, heads, f32, st);

@@ -54,22 +54,25 @@ bool wide_shape(int d, int h) { return d == kWideD && h == kWideH; }
 // fewer tokens than sub-blocks (then every product adds into slot 0).
 int64_t wide_splits(int64_t n_kv) { return n_kv >= kWideSub ? kWideSub : (n_kv > 0 ? 1 : 0); }
 
-size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q) {
+size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool ns) {
   const int64_t rows_kv = n_kv < kWideBlock ? n_kv : kWideBlock;
   const int64_t rows_q = n_q < kWideBlock ? n_q : kWideBlock;
   const int64_t rows = rows_kv > rows_q ? rows_kv : rows_q;
   const size_t bufs = round_up((size_t)rows * 3 * h * sizeof(uint16_t), 256);
   const size_t part = round_up((size_t)wide_splits(n_kv) * heads * 3 * (size_t)h * d * sizeof(float),
                                256);
-  return kWideLtWorkspace + bufs + part;
+  return kWideLtWorkspace + (ns ? round_up(wide_ns_bytes(heads, d, h), 256) : 0) + bufs + part;
 }
 
-WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv) {
+WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
+                   bool ns) {
   WideBufs w;
   char* p = (char*)ws + base;
   w.lt_ws = p;
   w.lt_ws_bytes = kWideLtWorkspace;
-  w.ab = (uint16_t*)(p + kWideLtWorkspace);
+  const size_t ns_bytes = ns ? round_up(wide_ns_bytes(heads, d, h), 256) : 0;
+  w.ns = ns ? p + kWideLtWorkspace : nullptr;
+  w.ab = (uint16_t*)(p + kWideLtWorkspace + ns_bytes);
   const size_t part = (size_t)wide_splits(n_kv) * heads * 3 * (size_t)h * d * sizeof(float);
   // partial sums at the end of the workspace, so the token-block buffers can
   // be sized by the larger of the update and apply counts

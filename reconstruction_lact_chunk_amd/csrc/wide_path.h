@@ -17,15 +17,24 @@ constexpr size_t kWideLtWorkspace = (size_t)64 << 20;  // GEMM library workspace
 struct WideBufs {
   void* lt_ws;        // GEMM library workspace
   size_t lt_ws_bytes;
+  void* ns;           // Newton-Schulz buffers (with that step rule), else null
   uint16_t* ab;       // token-block buffers: [rows][2 h] then [rows][h], bf16
   float* part;        // partial sums [kWideSub][heads][3][h d], at the end of the workspace
 };
 
 bool wide_shape(int d, int h);
 int64_t wide_splits(int64_t n_kv);
-// Workspace bytes beyond the two bf16 weight sets.
-size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q);
-WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv);
+// Workspace bytes beyond the two bf16 weight sets (ns: with the Newton-Schulz
+// step rule).
+size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool ns);
+WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
+                   bool ns);
+
+// Newton-Schulz of every matrix of the summed partials part0 ([heads][3][h d]),
+// in place; ns_ws holds wide_ns_bytes().
+size_t wide_ns_bytes(int heads, int d, int h);
+int wide_newton_schulz(float* part0, int heads, int d, int h, void* ns_ws, void* lt_ws,
+                       size_t lt_bytes, hipStream_t st);
 
 // Minus the chunk gradient over n tokens into w.part (one slot per block).
 int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* k,

@@ -153,6 +153,8 @@ hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
 // else split-bf16 products.
 hipError_t launch_newton_schulz(float* part, int splits, int heads, int d, int h, bool f32,
                                 hipStream_t st);
+// Adds the partial-sum slots of part ([splits][heads][3][h d]) into slot 0.
+hipError_t launch_sum_splits(float* part, int splits, int heads, int d, int h, hipStream_t st);
 
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
                              int d, int h, WSet w, hipStream_t st);

@@ -117,8 +117,13 @@ def test_full_width_shape_workspace_and_limits():
     assert ws_size(de, 0, 1000)[1] == base + 1000 * 3 * 2048 * 2
     assert ws_size(de, 200_000, 10)[1] == base + blk * 3 * 2048 * 2 + 8 * 3 * welems * 4
     assert ws_size(desc(heads=1, d=1024, h=2048, io=zm.F32), 10, 10)[0] == zm.ERR_UNSUPPORTED
-    assert ws_size(desc(heads=1, d=1024, h=2048, step_rule=zm.STEP_NEWTON_SCHULZ), 10, 10)[0] \
-        == zm.ERR_UNSUPPORTED
+    # the Newton-Schulz rule adds its iteration buffers (fp32 X, B X, A, A^2 and
+    # the bf16 planes of X and A for the three matrices, plus norm partials)
+    st, ns = ws_size(desc(heads=1, d=1024, h=2048, step_rule=zm.STEP_NEWTON_SCHULZ), 1000, 0)
+    assert st == zm.OK
+    M, N = 1024, 2048
+    ns_bytes = 2 * 3 * M * N * 4 + 2 * 3 * M * M * 4 + 2 * 3 * M * N * 2 + 2 * 3 * M * M * 2 + 768
+    assert ns == ws_size(de, 1000, 0)[1] + ns_bytes
     assert ws_size(desc(heads=1, d=1024, h=1024), 10, 10)[0] == zm.ERR_UNSUPPORTED
 
 

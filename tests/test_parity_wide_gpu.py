@@ -107,14 +107,15 @@ def test_wide_streaming_and_chunked():
         check(f"chunked {nm}", host(a), b, TOLB)
 
 
-def test_wide_bitwise_determinism():
-    say("case wide determinism n=70000")
+@pytest.mark.parametrize("rule", [zm.STEP_GRADIENT, zm.STEP_NEWTON_SCHULZ])
+def test_wide_bitwise_determinism(rule):
+    say(f"case wide determinism n=70000 rule={rule}")
     inp = wide_inputs(70_000, seed=45)
     t = inp.t
     a, oa = zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"], t["w3"],
-                            renorm=True)
+                            renorm=True, step_rule=rule)
     b, ob = zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"], t["w3"],
-                            renorm=True)
+                            renorm=True, step_rule=rule)
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
@@ -148,3 +149,28 @@ def test_wide_fw100_full_size_sampled():
     idx = torch.as_tensor(np.sort(rng.choice(wl.n_q, 1024, replace=False)), device="cuda")
     ref = oracle.apply(host(t["q"][idx]), host(g1), host(g2), host(g3))
     check("O sampled (1024 queries)", host(og[idx]), ref, TOLB)
+
+
+@pytest.mark.parametrize("n", [1, 3001, 20_000])
+def test_wide_newton_schulz(n):
+    """The review's update display after Eq. (3) on the full-width head: the
+    orthonormalisation of each 2048 x 1024 gradient as batched split-bf16 GEMMs."""
+    say(f"case wide Newton-Schulz n={n}")
+    inp = wide_inputs(n, seed=47 + n)
+    t = inp.t
+    w0 = [inp.np("w1"), inp.np("w2"), inp.np("w3")]
+    ns = zm.STEP_NEWTON_SCHULZ
+    (a1, a2, a3), o = zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"], t["w3"],
+                                      renorm=True, step_rule=ns)
+    (b1, b2, b3) = zm.update(t["k"], t["v"], t["eta"], t["w1"], t["w2"], t["w3"], renorm=False,
+                             step_rule=ns)
+    torch.cuda.synchronize()
+    ref_off = oracle.update(inp.np("k"), inp.np("v"), inp.np("eta"), *w0, renorm=False,
+                            step="newton_schulz")
+    ref_on = tuple(oracle.renorm_rows(w[0], r[0])[None] for w, r in zip(w0, ref_off))
+    for nm, a, b, r_on, r_off, w in zip(("W1", "W2", "W3"), (a1, a2, a3), (b1, b2, b3), ref_on,
+                                        ref_off, w0):
+        check(f"Delta {nm} = -NS(g)", host(b) - w, r_off - w, TOLB)
+        assert 0.4 < np.linalg.norm((r_off - w)[0], 2) < 1.3
+        check(f"{nm}_hat renorm=True", host(a), r_on, TOLB)
+    check("O renorm=True", host(o), oracle.apply(inp.np("q"), *ref_on), TOLB)
