@@ -11,28 +11,47 @@
 
 namespace zm {
 
-// One thread per element of the [H][h][d] index space.
+// One launch, two kinds of workgroup.  The first n_vec workgroups write the
+// scaled copies w1b, w3b, w2b, one thread per 4 consecutive elements (16-byte
+// loads, 8-byte stores).  The others write the transposed copy
+// w2tb[head][j][c] = W2[head][c][j] in 32 x 32 tiles through LDS, so both the
+// reads and the writes are row-contiguous.
 __global__ __launch_bounds__(256) void k_cast(const float* __restrict__ w1,
                                               const float* __restrict__ w2,
                                               const float* __restrict__ w3, int heads, int d,
-                                              int h, WSet out) {
-  const int64_t total = (int64_t)heads * h * d;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= total) return;
-  out.w1b[i] = to_bf16(kNegLog2e * w1[i]);
-  out.w3b[i] = to_bf16(w3[i]);
-  out.w2b[i] = to_bf16(kNegInvLog2e * w2[i]);  // same element count, [H][d][h] order
-  const int64_t hd = i / ((int64_t)h * d);
-  const int64_t rem = i - hd * h * d;
-  const int64_t j = rem / d, c = rem - j * d;
-  out.w2tb[i] = to_bf16(w2[(hd * d + c) * h + j]);  // w2tb[hd][j][c] = W2[hd][c][j]
+                                              int h, WSet out, int n_vec) {
+  if ((int)blockIdx.x < n_vec) {
+    const int64_t total = (int64_t)heads * h * d;
+    const int64_t i = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+    if (i >= total) return;
+    const f32x4 a = *(const f32x4*)(w1 + i), b = *(const f32x4*)(w3 + i), c = *(const f32x4*)(w2 + i);
+    *(u32x2*)(out.w1b + i) = u32x2{pack_bf16x2(kNegLog2e * a[0], kNegLog2e * a[1]),
+                                   pack_bf16x2(kNegLog2e * a[2], kNegLog2e * a[3])};
+    *(u32x2*)(out.w3b + i) = u32x2{pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+    *(u32x2*)(out.w2b + i) = u32x2{pack_bf16x2(kNegInvLog2e * c[0], kNegInvLog2e * c[1]),
+                                   pack_bf16x2(kNegInvLog2e * c[2], kNegInvLog2e * c[3])};
+    return;
+  }
+  __shared__ float tile[32][33];
+  const int t = blockIdx.x - n_vec;
+  const int tj = h / 32, tc = d / 32;
+  const int hd = t / (tj * tc), rem = t - hd * tj * tc;
+  const int c0 = 32 * (rem / tj), j0 = 32 * (rem % tj);
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const float* src = w2 + (int64_t)hd * d * h;
+  for (int r = ty; r < 32; r += 8) tile[r][tx] = src[(int64_t)(c0 + r) * h + j0 + tx];
+  __syncthreads();
+  uint16_t* dst = out.w2tb + (int64_t)hd * h * d;
+  for (int r = ty; r < 32; r += 8) dst[(int64_t)(j0 + r) * d + c0 + tx] = to_bf16(tile[tx][r]);
 }
 
 hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int heads, int d, int h,
                        WSet out, hipStream_t st) {
   const int64_t total = (int64_t)heads * h * d;
-  const unsigned blocks = (unsigned)ceil_div(total, 256);
-  hipLaunchKernelGGL(k_cast, dim3(blocks), dim3(256), 0, st, w1, w2, w3, heads, d, h, out);
+  const int n_vec = (int)ceil_div(total / 4, 256);
+  const int n_tr = heads * (h / 32) * (d / 32);
+  hipLaunchKernelGGL(k_cast, dim3(n_vec + n_tr), dim3(256), 0, st, w1, w2, w3, heads, d, h, out,
+                     n_vec);
   return hipGetLastError();
 }
 
