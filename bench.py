@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--no-renorm", action="store_true")
     p.add_argument("--step-rule", default="gradient", choices=["gradient", "newton_schulz"],
                    help="the update's step: W - g (default) or W - NewtonSchulz(g)")
+    p.add_argument("--graph", action="store_true",
+                   help="also time the step captured once in a HIP graph and replayed (no host "
+                        "launch overhead per call)")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a known-size "
                         "reference dispatch for scaling HBM counters)")
@@ -225,6 +228,31 @@ def main():
     wall = time.perf_counter() - wall0
     ms = t_start.elapsed_time(t_end) / K
 
+    graph_ms = None
+    if args.graph:
+        # one step captured on a side stream of default priority, then replayed
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(K):
+            g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / K
+        log(f"graph replay: {graph_ms:.4f} ms per step")
+
     n_tok = wl.n_kv
     flops_upd = wl.flops_per_token_update() * wl.n_kv
     flops_app = wl.flops_per_token_apply() * wl.n_q
@@ -338,6 +366,10 @@ def main():
         "step_rule": args.step_rule,
     }
     result["wall_s_timed"] = round(wall, 3)
+    if graph_ms is not None:
+        result["graph_ms_per_step"] = round(graph_ms, 4)
+        result["graph_value"] = (n_tok / (graph_ms / wl.layers / 1e3) if not wl.streaming
+                                 else n_tok / (graph_ms / 1e3))
 
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens

@@ -361,3 +361,47 @@ def test_stream256_full_size_per_step():
     check("frame 3 O (chain)", outs[3], routs[3], TOL["bf16"])
     for nm, a, b in zip(("W1", "W2", "W3"), after[3], rw):
         check(f"{nm} after 4 frames (chain)", a, b, TOL["bf16"])
+
+
+def test_graph_replay_matches_eager():
+    """The library only enqueues kernels on the caller's stream (no allocation,
+    no memset, no synchronisation), so a call can be captured in a HIP graph.
+    The graph is replayed several times with eager work and synchronisations in
+    between, and every replay must equal the eager result bitwise."""
+    say("case HIP graph capture and replay of update_apply and stream_step")
+    inp = Inputs(seed=61, n=2748)
+    t = inp.t
+    ws = torch.empty(zm.workspace_size(zm.make_desc(t["w1"], t["w2"], t["w3"], zm.BF16, True,
+                                                    t["q"], t["k"]), 2748, 2748),
+                     dtype=torch.uint8, device="cuda")
+    w_out = [torch.empty_like(w) for w in (t["w1"], t["w2"], t["w3"])]
+    o = torch.empty_like(t["q"])
+
+    def call():
+        zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"], t["w3"], renorm=True,
+                        w_out=w_out, out=o, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref_w = [x.clone() for x in w_out]
+    ref_o = o.clone()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call()
+    for r in range(3):
+        for x in w_out:
+            x.zero_()
+        o.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(w_out, ref_w):
+            assert torch.equal(x, y), r
+        assert torch.equal(o, ref_o), r
+        _ = (t["q"].float() * 2).sum().item()  # eager work between replays
