@@ -405,3 +405,10 @@ def test_graph_replay_matches_eager():
             assert torch.equal(x, y), r
         assert torch.equal(o, ref_o), r
         _ = (t["q"].float() * 2).sum().item()  # eager work between replays
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_max_heads(io):
+    """64 heads (the largest count accepted) of d 64 / hidden 128."""
+    say(f"case 64 heads io={io}")
+    full_parity(Inputs(seed=62, n=777, heads=64, d=64, h=128, io=io), TOL[io])

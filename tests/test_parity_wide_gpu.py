@@ -174,3 +174,23 @@ def test_wide_newton_schulz(n):
         assert 0.4 < np.linalg.norm((r_off - w)[0], 2) < 1.3
         check(f"{nm}_hat renorm=True", host(a), r_on, TOLB)
     check("O renorm=True", host(o), oracle.apply(inp.np("q"), *ref_on), TOLB)
+
+
+@pytest.mark.parametrize("rule", ["gradient", "newton_schulz"])
+def test_wide_two_heads(rule):
+    """Two full-width heads: the forward products per head (the [W1; W3]
+    single-GEMM form needs one head) and a batch of six matrices in the
+    Newton-Schulz iteration."""
+    say(f"case wide two heads rule={rule}")
+    inp = Inputs(seed=48, n=900, heads=2, d=D, h=H_, eta_scale=10.0)
+    t = inp.t
+    code = zm.STEP_NEWTON_SCHULZ if rule == "newton_schulz" else zm.STEP_GRADIENT
+    w0 = [inp.np("w1"), inp.np("w2"), inp.np("w3")]
+    (a1, a2, a3), o = zm.update_apply(t["k"], t["v"], t["eta"], t["q"], t["w1"], t["w2"], t["w3"],
+                                      renorm=False, step_rule=code)
+    torch.cuda.synchronize()
+    ref, ro = oracle.update_apply(inp.np("k"), inp.np("v"), inp.np("eta"), inp.np("q"), *w0,
+                                  renorm=False, step=rule)
+    for nm, a, b, w in zip(("W1", "W2", "W3"), (a1, a2, a3), ref, w0):
+        check(f"Delta {nm}", host(a) - w, b - w, TOLB)
+    check("O", host(o), ro, TOLB)
