@@ -88,15 +88,12 @@ def test_bad_image_size():
 
 def test_full_width_workloads_match_the_notes_state_size():
     """The full-width head is the notes' fast-weight state: d = 1024, hidden
-    2048, 6 d^2 = 6,291,456 parameters per layer (golden/page_figures.json)."""
-    import json
-    import os
-    fig = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
-    st = fig["state_size"]
+    2048, 6 d^2 = 6,291,456 parameters per layer."""
+    st = golden()["state_size"]
     for name in ("fw8", "fw100", "fw700"):
-        wl = WL.WORKLOADS[name]
+        wl = W.WORKLOADS[name]
         assert (wl.heads, wl.d_head, wl.d_hidden) == (1, st["d"], st["hidden"])
         assert 3 * wl.d_head * wl.d_hidden * wl.heads == st["params_per_layer"] == 6 * st["d"] ** 2
         assert wl.tokens_per_frame == 1374
     # the 8-head shape splits the same model width
-    assert WL.WORKLOADS["f700"].heads * WL.WORKLOADS["f700"].d_head == st["d"]
+    assert W.WORKLOADS["f700"].heads * W.WORKLOADS["f700"].d_head == st["d"]
