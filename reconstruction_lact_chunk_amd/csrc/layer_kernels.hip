@@ -25,10 +25,13 @@ __global__ __launch_bounds__(256) void k_eta_from_logits(const uint16_t* __restr
   eta[i] = scale / (1.f + __expf(-z));
 }
 
-// One wave per token: lanes take 8 consecutive elements at a time (16-byte
-// loads) across the width; the sum of squares is a wave butterfly, so every
-// lane holds the same bits.  op, g: bf16 rows (strides ldo, ldg); o: bf16 rows
-// (stride ldout).  width is a multiple of 8.
+// One wave per token: lane l holds the 16-byte pieces c = 8 l + 512 i
+// (i < NC) of its row of o' and of g, loaded once into registers (NC 512-wide
+// pieces cover the width).  The sum of squares adds the pieces in order and
+// ends with a wave butterfly, so every lane holds the same bits.  op, g: bf16
+// rows (strides ldo, ldg); o: bf16 rows (stride ldout).  width is a multiple
+// of 8 and at most 512 NC.
+template <int NC>
 __global__ __launch_bounds__(256) void k_rmsnorm_gate(const uint16_t* __restrict__ op,
                                                       int64_t ldo, const uint16_t* __restrict__ g,
                                                       int64_t ldg, const float* __restrict__ gamma,
@@ -38,12 +41,25 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gate(const uint16_t* __restrict
   if (t >= n) return;
   const int lane = threadIdx.x & 63;
   const uint16_t* orow = op + t * ldo;
+  const uint16_t* grow = g + t * ldg;
+  u32x4 ov[NC], gv[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 8 * lane + 512 * i;
+    if (c < width) {
+      ov[i] = *(const u32x4*)(orow + c);
+      gv[i] = *(const u32x4*)(grow + c);
+    } else {
+      ov[i] = u32x4{0u, 0u, 0u, 0u};
+      gv[i] = ov[i];
+    }
+  }
   float ss = 0.f;
-  for (int c = 8 * lane; c < width; c += 512) {
-    const u32x4 w = *(const u32x4*)(orow + c);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float lo = bf16lo(w[q]), hi = bf16hi(w[q]);
+      const float lo = bf16lo(ov[i][q]), hi = bf16hi(ov[i][q]);
       ss = fmaf(lo, lo, ss);
       ss = fmaf(hi, hi, ss);
     }
@@ -51,20 +67,20 @@ __global__ __launch_bounds__(256) void k_rmsnorm_gate(const uint16_t* __restrict
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
   const float r = 1.f / sqrtf(ss / (float)width + eps);
-  const uint16_t* grow = g + t * ldg;
   uint16_t* out = o + t * ldout;
-  for (int c = 8 * lane; c < width; c += 512) {
-    const u32x4 w = *(const u32x4*)(orow + c);
-    const u32x4 gw = *(const u32x4*)(grow + c);
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const int c = 8 * lane + 512 * i;
+    if (c >= width) break;
     const f32x4 ga = *(const f32x4*)(gamma + c), gb = *(const f32x4*)(gamma + c + 4);
     u32x4 res;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float v[2], gg[2];
-      v[0] = bf16lo(w[q]);
-      v[1] = bf16hi(w[q]);
-      gg[0] = bf16lo(gw[q]);
-      gg[1] = bf16hi(gw[q]);
+      v[0] = bf16lo(ov[i][q]);
+      v[1] = bf16hi(ov[i][q]);
+      gg[0] = bf16lo(gv[i][q]);
+      gg[1] = bf16hi(gv[i][q]);
       float out2[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -91,8 +107,17 @@ hipError_t launch_rmsnorm_gate(const uint16_t* op, int64_t ldo, const uint16_t* 
                                const float* gamma, float eps, uint16_t* o, int64_t ldout,
                                int width, int64_t n, hipStream_t st) {
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rmsnorm_gate, dim3((unsigned)ceil_div(n, 4)), dim3(256), 0, st, op, ldo, g,
-                     ldg, gamma, eps, o, ldout, width, n);
+  const dim3 grid((unsigned)ceil_div(n, 4));
+#define ZM_LAUNCH_GATE(NC)                                                                    \
+  hipLaunchKernelGGL((k_rmsnorm_gate<NC>), grid, dim3(256), 0, st, op, ldo, g, ldg, gamma, eps, \
+                     o, ldout, width, n)
+  if (width <= 512) ZM_LAUNCH_GATE(1);
+  else if (width <= 1024) ZM_LAUNCH_GATE(2);
+  else if (width <= 2048) ZM_LAUNCH_GATE(4);
+  else if (width <= 4096) ZM_LAUNCH_GATE(8);
+  else if (width <= 8192) ZM_LAUNCH_GATE(16);
+  else return hipErrorInvalidValue;
+#undef ZM_LAUNCH_GATE
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10100
+    assert zm.version() == 10101
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -238,11 +238,14 @@ def test_layer_workspace_and_argument_checks():
     st, need = layer_ws(de, lw, 1000)
     assert st == zm.OK
     # projection rows (3 H d + H rounded to 8 bf16), eta, the GEMM workspace, the TTT workspace
-    ttt = ws_size(desc(ld=3080), 1000, 1000)[1]
-    rows = (1000 * 3080 * 2 + 255) // 256 * 256
+    ttt = ws_size(desc(ld=3136), 1000, 1000)[1]
+    rows = 1000 * 3136 * 2                        # 3 H d + H = 3080 columns, rows padded to 64
     eta = (1000 * 8 * 4 + 255) // 256 * 256
     assert need == rows + eta + (64 << 20) + ttt
     assert layer_ws(desc(io=zm.F32), lw, 10)[0] == zm.ERR_UNSUPPORTED
+    # layer width H d: 8 full-width heads (8192) are accepted, 9 (9216) are not
+    assert layer_ws(desc(heads=8, d=1024, h=2048, ld=8192), lw, 10)[0] == zm.OK
+    assert layer_ws(desc(heads=9, d=1024, h=2048, ld=9216), lw, 10)[0] == zm.ERR_UNSUPPORTED
     for bad in (lw_struct(d_in=12), lw_struct(d_in=0), lw_struct(eta_scale=-1.0),
                 lw_struct(eps=0.0), lw_struct(reserved=1), lw_struct(w_in=None),
                 lw_struct(gamma=P((1 << 20) + 4))):
