@@ -156,7 +156,9 @@ ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
  * Reconstruction, Eq. (6)).  w1, w2, w3 hold the state W(t-1) on entry and
  * W(t) on return (updated in place).  q, k, v: [n_frame, heads, d_head];
  * eta: [n_frame, heads]; o receives f_{W(t-1)}(q) (APPLY_THEN_UPDATE) or
- * f_{W(t)}(q) (UPDATE_THEN_APPLY). */
+ * f_{W(t)}(q) (UPDATE_THEN_APPLY).  o must not overlap q, k, v or eta: with
+ * APPLY_THEN_UPDATE and bf16 io the read and the update's partial sums run
+ * side by side in one launch. */
 ZM_API int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame,
                        const void* q, const void* k, const void* v, const float* eta,
                        float* w1, float* w2, float* w3, void* o,
@@ -177,8 +179,9 @@ ZM_API int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_fram
  * rows.
  * offsets: host memory, n_chunks + 1 int64, offsets[0] = 0, non-decreasing;
  * n_chunks in [0, 2^24].  Empty chunks are skipped.
- * q, k, v, o: [n, heads, d_head]; eta: [n, heads].  w1, w2, w3 hold the state
- * and are updated in place.  The workspace must hold
+ * q, k, v, o: [n, heads, d_head]; eta: [n, heads]; o must not overlap q, k,
+ * v or eta (as for zm_ttt_stream_step).  w1, w2, w3 hold the state and are
+ * updated in place.  The workspace must hold
  * zm_ttt_workspace_size(desc, L, L) bytes, L the longest chunk.  Equivalent to
  * one zm_ttt_stream_step per chunk (extended by the mask and inner steps). */
 ZM_API int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks,
@@ -240,7 +243,9 @@ ZM_API int zm_ttt_version(void);
  * (0 weight cast, 1 update partial sums, 2 reduce/step/renorm, 3 apply,
  * 4 Newton-Schulz, 5 input projections and rate, 6 output gate) records
  * events[2s] before and events[2s+1] after itself on the launch stream, for
- * each non-NULL slot.  The events are hipEvent_t handles passed as void*;
+ * each non-NULL slot.  Where a chunk's read and its update's partial sums
+ * share one launch (bf16 APPLY_THEN_UPDATE), the events of stages 1 and 3
+ * both bracket that launch.  The events are hipEvent_t handles passed as void*;
  * n_events must be 8 (stages 0-3), 10 (0-4) or 14 (0-6) (or 0 with
  * events == NULL to switch off).  Process-wide setting; not for concurrent use
  * from several threads. */

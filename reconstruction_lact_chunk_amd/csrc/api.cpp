@@ -171,6 +171,10 @@ int check_ws(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q, void* ws, size_t w
     }                                                                               \
   } while (0)
 
+int finish_update(const zm_ttt_desc* d, int64_t n, const float* w1, const float* w2,
+                  const float* w3, float* o1, float* o2, float* o3, float* part, int splits,
+                  const WSet* emit, hipStream_t st);
+
 // The update part shared by update, update_apply and stream_step: partial
 // sums over n_kv tokens, then the reduce/step/renorm into w*_out.  When
 // emit is non-null the reduce also writes the bf16 copies of W_hat there.
@@ -222,7 +226,15 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
                                d->d_head, d->d_hidden, w1, w2, w3, part, L.plan, st));
     }
   }
-  int splits = L.plan.splits;
+  return finish_update(d, n, w1, w2, w3, o1, o2, o3, part, L.plan.splits, emit, st);
+}
+
+// The rest of a narrow-head update once the partial sums of n tokens are in
+// part ([splits][heads][3][h d]): the Newton-Schulz step if asked for, then
+// the reduce/step/renorm into o*.
+int finish_update(const zm_ttt_desc* d, int64_t n, const float* w1, const float* w2,
+                  const float* w3, float* o1, float* o2, float* o3, float* part, int splits,
+                  const WSet* emit, hipStream_t st) {
   if (n > 0 && d->step_rule == ZM_STEP_NEWTON_SCHULZ) {
     // partials -> slot 0 -> NewtonSchulz(minus the gradient), in place
     Scoped ns(kStageNewtonSchulz, st);
@@ -278,8 +290,24 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
       Scoped s(kStageCast, st);
       ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
     }
-    ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, ws, st));
-    for (int i = 0; i < updates; ++i)
+    int first = 0;
+    if (bf16 && !is_wide(d) && updates > 0 && n > 0) {
+      // The read and the first update's partial sums use only the incoming W:
+      // one launch for both (both stages' profile events bracket it).
+      float* part = (float*)((char*)ws.p + L.part);
+      {
+        Scoped su(kStageUpdate, st);
+        Scoped sa(kStageApply, st);
+        ZM_HIP(launch_frame_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta,
+                                 (uint16_t*)o, n, d->ld_tok, d->heads, d->d_head, d->d_hidden, a,
+                                 part, L.plan, st));
+      }
+      ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits, nullptr, st));
+      first = 1;
+    } else {
+      ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, ws, st));
+    }
+    for (int i = first; i < updates; ++i)
       ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws, nullptr, bf16 && i == 0, st));
     return ZM_OK;
   }

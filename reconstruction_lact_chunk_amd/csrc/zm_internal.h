@@ -124,10 +124,15 @@ struct ApplyPlan {
   int64_t chunk;
 };
 
-inline ApplyPlan plan_apply(int64_t n, int heads) {
+// Up to `wgs` workgroups (by default one per compute unit).  A launch shared
+// with update workgroups passes the compute units those leave free; fewer
+// than one per head falls back to the default.  The apply is per token, so
+// its output does not depend on the split.
+inline ApplyPlan plan_apply(int64_t n, int heads, int64_t wgs = kTargetWgs) {
   ApplyPlan p{0, 0};
   if (n <= 0) return p;
-  int64_t target = kTargetWgs / heads;
+  if (wgs < heads) wgs = kTargetWgs;
+  int64_t target = wgs / heads;
   if (target < 1) target = 1;
   const int64_t tiles = ceil_div(n, kTok);
   int64_t s = tiles < target ? tiles : target;
@@ -158,6 +163,12 @@ hipError_t launch_sum_splits(float* part, int splits, int heads, int d, int h, h
 
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
                              int d, int h, WSet w, hipStream_t st);
+
+// The apply of n queries and the update partial sums of the same n tokens,
+// both through the bf16 set w, in one launch (frame_bf16.hip).
+hipError_t launch_frame_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                             const float* eta, uint16_t* o, int64_t n, int64_t ld, int heads,
+                             int d, int h, WSet w, float* part, UpdatePlan plan, hipStream_t st);
 
 hipError_t launch_update_f32(const float* k, const float* v, const float* eta, int64_t n,
                              int64_t ld, int heads, int d, int h, const float* w1,
