@@ -30,7 +30,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PEAK_F32_VALU_TFLOPS = 157.3   # MI355X fp32 vector peak
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = {"update": "update_bf16.hip", "apply": "apply_bf16.hip"}
+# the source files of each roofline kernel (body header, then kernel entry)
+KERNEL_SOURCES = {"update": ("update_bf16.h", "update_bf16.hip"),
+                  "apply": ("apply_bf16.h", "apply_bf16.hip")}
 
 
 def log(*a):
@@ -62,10 +64,12 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(name):
-    path = os.path.join(ROOT, "reconstruction_lact_chunk_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(names):
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "reconstruction_lact_chunk_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def stored_traffic(kernel, per_launch_units):
