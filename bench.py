@@ -45,14 +45,17 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="f700",
-                   choices=["f700", "f100", "f8", "f700x24", "stream256", "fw8", "fw100", "fw700",
-                            "layer700"])
+                   choices=["f700", "f100", "f8", "f700x24", "stream256", "chunked256", "fw8",
+                            "fw100", "fw700", "layer700"])
     p.add_argument("--seed", type=int, default=4)
     p.add_argument("--cpu-sample-tokens", type=int, default=0,
                    help="tokens for the oracle baseline (default: 262144 at the 8-head shape, "
                         "131072 at the full-width shape; 10-15 s of host time either way)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-renorm", action="store_true")
+    p.add_argument("--order", default=None, choices=["apply_then_update", "update_then_apply"],
+                   help="read/write order of the streaming and chunked workloads (default: "
+                        "apply_then_update per streamed frame, update_then_apply per chunk)")
     p.add_argument("--step-rule", default="gradient", choices=["gradient", "newton_schulz"],
                    help="the update's step: W - g (default) or W - NewtonSchulz(g)")
     p.add_argument("--graph", action="store_true",
@@ -151,6 +154,8 @@ def main():
     whole = wl.name.startswith("layer")
     renorm = not args.no_renorm and wl.renorm
     rule = zm.STEP_NEWTON_SCHULZ if args.step_rule == "newton_schulz" else zm.STEP_GRADIENT
+    order_name = args.order or ("update_then_apply" if wl.chunked else "apply_then_update")
+    order = zm.UPDATE_THEN_APPLY if order_name == "update_then_apply" else zm.APPLY_THEN_UPDATE
     log(f"workload {wl.name}: n_kv={wl.n_kv} n_q={wl.n_q} H={wl.heads} d={wl.d_head} "
         f"h={wl.d_hidden} layers={wl.layers}")
     if args.copy_calibration_mib > 0:
@@ -194,11 +199,18 @@ def main():
         del ws
 
     def step(prof=None):
+        if wl.chunked:
+            w = [t.clone() for t in ws_layers[0]]
+            offsets = [0] + [e for _, e in WL.frame_slices(wl)]
+            zm.chunked(x["q"], x["k"], x["v"], x["eta"], offsets, *w, renorm=renorm, order=order,
+                       out=o, workspace=ws, step_rule=rule)
+            return
         if wl.streaming:
             w = [t.clone() for t in ws_layers[0]]
             for (s, e) in WL.frame_slices(wl):
                 zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
-                               renorm=renorm, out=o[s:e], workspace=ws, step_rule=rule)
+                               renorm=renorm, order=order, out=o[s:e], workspace=ws,
+                               step_rule=rule)
             return
         for li, wl_w in enumerate(ws_layers):
             if prof is not None:
@@ -357,6 +369,8 @@ def main():
                      "f8": "8 frames x 1374 tokens",
                      "f700x24": "700-frame layer x 24 layers with fresh weights per layer",
                      "stream256": "256 frames x 1374 tokens, one streaming step per frame",
+                     "chunked256": "256 frames x 1374 tokens as the 256 chunks of one "
+                                   "zm_ttt_chunked call",
                      "fw8": "8 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
                      "fw100": "100 frames x 1374 tokens, one full-width head (d 1024, hidden 2048)",
                      "fw700": "700 frames x 1374 tokens, one full-width head (d 1024, hidden "
@@ -369,6 +383,8 @@ def main():
         "io": "bf16 tokens, fp32 fast weights, fp32 accumulation",
         "step_rule": args.step_rule,
     }
+    if wl.streaming:
+        result["config"]["order"] = order_name
     result["wall_s_timed"] = round(wall, 3)
     if graph_ms is not None:
         result["graph_ms_per_step"] = round(graph_ms, 4)

@@ -298,9 +298,9 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
       {
         Scoped su(kStageUpdate, st);
         Scoped sa(kStageApply, st);
-        ZM_HIP(launch_frame_bf16((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, eta,
-                                 (uint16_t*)o, n, d->ld_tok, d->heads, d->d_head, d->d_hidden, a,
-                                 part, L.plan, st));
+        ZM_HIP(launch_frame_bf16((const uint16_t*)q, (uint16_t*)o, n, (const uint16_t*)k,
+                                 (const uint16_t*)v, eta, n, d->ld_tok, d->heads, d->d_head,
+                                 d->d_hidden, a, part, L.plan, st));
       }
       ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits, nullptr, st));
       first = 1;
@@ -319,6 +319,80 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
 }
 
 inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2 : 4; }
+
+// zm_ttt_chunked for the narrow heads with bf16 io.  Between chunks W's bf16
+// copy stays current in set a: it is cast once, and every reduce re-emits it
+// with the stepped W.  Each read shares a launch with an update step that
+// uses the same W.  With APPLY_THEN_UPDATE, chunk c's read goes with its own
+// first update.  With UPDATE_THEN_APPLY, chunk c's read waits for the first
+// update of the next updated chunk, which starts from the same W.  Reads of
+// chunks without an update run alone.  Every kernel sees the inputs of the
+// per-chunk routine, so the results are bitwise those of run_chunk.
+int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const int64_t* offsets,
+                     const uint8_t* update_mask, int inner, const char* q, const char* k,
+                     const char* v, const float* eta, float* w1, float* w2, float* w3, char* o,
+                     Ws ws, hipStream_t st) {
+  const Layout L0 = layout(d, 0, 0);  // set and partial-sum offsets do not depend on n
+  const WSet a = carve_set(ws.p, L0.set_a, (size_t)d->heads * d->d_hidden * d->d_head);
+  float* part = (float*)((char*)ws.p + L0.part);
+  const size_t row = (size_t)d->ld_tok * sizeof(uint16_t);
+  const int hd = d->heads, dh = d->d_head, hh = d->d_hidden;
+  auto tok = [&](const char* base, int64_t c) { return (const uint16_t*)(base + offsets[c] * row); };
+  auto len = [&](int64_t c) { return offsets[c + 1] - offsets[c]; };
+  auto read = [&](int64_t c) {  // o_c = f_W(q_c) through set a
+    Scoped s(kStageApply, st);
+    return launch_apply_bf16(tok(q, c), (uint16_t*)(o + offsets[c] * row), len(c), d->ld_tok, hd,
+                             dh, hh, a, st);
+  };
+  // One update step on chunk c from the W in set a (W <- step, a <- bf16(W)),
+  // with chunk rc's read in the same launch when rc >= 0.
+  auto step = [&](int64_t c, int64_t rc) -> int {
+    const UpdatePlan plan = plan_update(len(c), hd, hh);
+    const float* e = eta + offsets[c] * hd;
+    {
+      Scoped su(kStageUpdate, st);
+      if (rc >= 0) {
+        Scoped sa(kStageApply, st);
+        ZM_HIP(launch_frame_bf16(tok(q, rc), (uint16_t*)(o + offsets[rc] * row), len(rc), tok(k, c),
+                                 tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part, plan, st));
+      } else {
+        ZM_HIP(launch_update_bf16(tok(k, c), tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part,
+                                  plan, st));
+      }
+    }
+    return finish_update(d, len(c), w1, w2, w3, w1, w2, w3, part, plan.splits, &a, st);
+  };
+  bool cast = false;
+  int64_t pending = -1;  // UPDATE_THEN_APPLY: a chunk whose read is still to run
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    if (len(c) == 0) continue;
+    const bool upd = update_mask == nullptr || update_mask[c] != 0;
+    if (!cast) {
+      Scoped s(kStageCast, st);
+      ZM_HIP(launch_cast(w1, w2, w3, hd, dh, hh, a, st));
+      cast = true;
+    }
+    if (order == ZM_APPLY_THEN_UPDATE) {
+      if (!upd) {
+        ZM_HIP(read(c));
+        continue;
+      }
+      ZM_TRY(step(c, c));
+      for (int i = 1; i < inner; ++i) ZM_TRY(step(c, -1));
+      continue;
+    }
+    if (!upd) {  // W does not change: the waiting read and this one use it as it is
+      if (pending >= 0) ZM_HIP(read(pending));
+      pending = c;
+      continue;
+    }
+    ZM_TRY(step(c, pending));
+    for (int i = 1; i < inner; ++i) ZM_TRY(step(c, -1));
+    pending = c;
+  }
+  if (pending >= 0) ZM_HIP(read(pending));
+  return ZM_OK;
+}
 
 // Workspace of zm_ttt_layer: the projection rows Y [n][ldy] bf16 (q | k | v |
 // rate logits; later o' in the k columns and W_g o' in the v columns), eta,
@@ -563,6 +637,10 @@ int zm_ttt_chunked(const zm_ttt_desc* desc, int order, int64_t n_chunks, const i
   ZM_TRY(check_weights(w1, w2, w3));
   ZM_TRY(check_ws(desc, longest, longest, workspace, workspace_bytes));
   hipStream_t st = (hipStream_t)stream;
+  if (desc->io_dtype == ZM_BF16 && !is_wide(desc))
+    return run_chunked_bf16(desc, order, n_chunks, offsets, update_mask, inner_steps,
+                            (const char*)q, (const char*)k, (const char*)v, eta, w1, w2, w3,
+                            (char*)o, Ws{workspace, workspace_bytes}, st);
   const size_t row = (size_t)desc->ld_tok * io_bytes(desc);  // bytes per token row
   for (int64_t c = 0; c < n_chunks; ++c) {
     const int64_t s0 = offsets[c], len = offsets[c + 1] - s0;

@@ -164,11 +164,13 @@ hipError_t launch_sum_splits(float* part, int splits, int heads, int d, int h, h
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
                              int d, int h, WSet w, hipStream_t st);
 
-// The apply of n queries and the update partial sums of the same n tokens,
-// both through the bf16 set w, in one launch (frame_bf16.hip).
-hipError_t launch_frame_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const float* eta, uint16_t* o, int64_t n, int64_t ld, int heads,
-                             int d, int h, WSet w, float* part, UpdatePlan plan, hipStream_t st);
+// The apply of n_q queries and the update partial sums over n_kv tokens
+// (plan = plan_update(n_kv, ...)), both through the bf16 set w, in one launch
+// (frame_bf16.hip).  n_q, n_kv > 0; q / o and k / v rows share the stride ld.
+hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const uint16_t* k,
+                             const uint16_t* v, const float* eta, int64_t n_kv, int64_t ld,
+                             int heads, int d, int h, WSet w, float* part, UpdatePlan plan,
+                             hipStream_t st);
 
 hipError_t launch_update_f32(const float* k, const float* v, const float* eta, int64_t n,
                              int64_t ld, int heads, int d, int h, const float* w1,

@@ -62,3 +62,40 @@ def test_chunked_inner_steps_after_the_shared_launch():
     assert torch.equal(o, torch.cat(outs))
     for a, b in zip(state, ref):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("order", [zm.APPLY_THEN_UPDATE, zm.UPDATE_THEN_APPLY])
+@pytest.mark.parametrize("mask,inner,rule", [
+    (None, 1, zm.STEP_GRADIENT),
+    ([1, 0, 1, 1, 1, 0], 1, zm.STEP_GRADIENT),
+    ([0, 1, 1, 0, 1, 1], 2, zm.STEP_GRADIENT),
+    ([1, 1, 0, 1, 0, 0], 1, zm.STEP_NEWTON_SCHULZ),
+])
+def test_chunked_equals_separate_calls(order, mask, inner, rule):
+    """zm_ttt_chunked keeps W's bf16 copy across chunks and pairs each read with
+    an update step that uses the same W; every result must equal a plain loop
+    of zm_ttt_update / zm_ttt_apply calls, bit for bit (ragged chunks, an empty
+    chunk, skipped updates, inner steps)."""
+    offsets = [0, 1374, 2074, 2074, 2107, 4855, 4984]
+    say(f"case chunked vs separate calls order={order} mask={mask} inner={inner} rule={rule}")
+    q, k, v, eta, w = tensors(offsets[-1], 8, 128, 256, seed=63)
+    state = [t.clone() for t in w]
+    o = zm.chunked(q, k, v, eta, offsets, *state, renorm=True, order=order, update_mask=mask,
+                   inner_steps=inner, step_rule=rule)
+    ref = [t.clone() for t in w]
+    o_ref = torch.zeros_like(o)
+    for c in range(len(offsets) - 1):
+        s, e = offsets[c], offsets[c + 1]
+        if s == e:
+            continue
+        upd = mask is None or mask[c]
+        if order == zm.APPLY_THEN_UPDATE:
+            o_ref[s:e] = zm.apply(q[s:e], *ref)
+        for _ in range(inner if upd else 0):
+            ref = list(zm.update(k[s:e], v[s:e], eta[s:e], *ref, renorm=True, step_rule=rule))
+        if order == zm.UPDATE_THEN_APPLY:
+            o_ref[s:e] = zm.apply(q[s:e], *ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in zip(state, ref):
+        assert torch.equal(a, b)

@@ -48,7 +48,8 @@ class Workload:
     renorm: bool
     extra_queries: int = 0      # target-view ray queries read after the update
     layers: int = 1
-    streaming: bool = False
+    streaming: bool = False     # one frame at a time
+    chunked: bool = False       # the frames as the chunks of one multi-chunk call
     description: str = field(default="", compare=False)
 
     @property
@@ -87,6 +88,9 @@ WORKLOADS = {
                         description="the 700-frame layer repeated 24 times"),
     "stream256": Workload("stream256", 256, 518, 8, 128, 256, "bf16", True, streaming=True,
                           description="256 frames fed one at a time"),
+    "chunked256": Workload("chunked256", 256, 518, 8, 128, 256, "bf16", True, streaming=True,
+                           chunked=True,
+                           description="the 256 frames as 256 chunks of one multi-chunk call"),
     # the full-width fast weight: one head of the whole model width 1024 with
     # hidden 2048 (a 6 d^2 state, d = 1024)
     "fw8": Workload("fw8", 8, 518, 1, 1024, 2048, "bf16", True,
@@ -101,6 +105,7 @@ WORKLOADS = {
                          description="700 frames x 1374 tokens through the whole layer"),
 }
 CONFIG_IDS = {"tiny": 1, "f8": 2, "f100": 3, "f700": 4, "f700x24": 4, "stream256": 5,
+              "chunked256": 5,
               "fw8": 6, "fw100": 7, "fw700": 8, "layer700": 9}
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_ETA, STREAM_QX = 1, 2, 3, 4, 5
