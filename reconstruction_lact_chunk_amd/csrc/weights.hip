@@ -96,12 +96,16 @@ __device__ __forceinline__ void reduce_row4(const float* __restrict__ part, int 
   *(f32x4*)(wout) = nv;
 }
 
+// Each workgroup covers 1024 consecutive elements, which lie in one matrix
+// (h d is a multiple of 1024 for every supported shape); the grid has no
+// partial workgroup.
 template <int D, int HID>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int splits,
                                                 int heads, const float* w1, const float* w2,
                                                 const float* w3, float* o1, float* o2, float* o3,
                                                 int renorm, WSet ob, int emit_bf16) {
   constexpr int64_t HD = (int64_t)HID * D;
+  static_assert(HD % 1024 == 0 && (HID == 128 || HID == 256), "workgroups within one matrix");
   const int64_t e = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);  // element index
   if (e >= (int64_t)heads * 3 * HD) return;
   const int64_t head = e / (3 * HD);
@@ -129,10 +133,28 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, 
       u32x2 pk = {pack_bf16x2(kNegInvLog2e * nv[0], kNegInvLog2e * nv[1]),
                   pack_bf16x2(kNegInvLog2e * nv[2], kNegInvLog2e * nv[3])};
       *(u32x2*)(ob.w2b + off) = pk;
-      // transposed copy: w2tb[head][j][c] = W2[head][c][j]
-      const int64_t c = local / HID, j = local - c * HID;
+      // Transposed copy w2tb[head][j][c] = W2[head][c][j] through LDS: the
+      // workgroup's 1024 elements are RW whole rows c0 .. c0 + RW - 1 of W2
+      // (a row block starts on a multiple of 1024 elements), so thread j
+      // writes rows' column j as one RW-element piece of w2tb row j.
+      constexpr int RW = 1024 / HID;
+      __shared__ float tr[1024];
+      *(f32x4*)&tr[4 * threadIdx.x] = nv;
+      __syncthreads();
+      if ((int)threadIdx.x < HID) {
+        const int64_t c0 = (local - 4 * (int64_t)threadIdx.x) / HID;
+        unsigned pk2[RW / 2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ob.w2tb[(head * HID + j + q) * D + c] = to_bf16(nv[q]);
+        for (int r = 0; r < RW; r += 2)
+          pk2[r / 2] = (unsigned)to_bf16(tr[r * HID + threadIdx.x]) |
+                       ((unsigned)to_bf16(tr[(r + 1) * HID + threadIdx.x]) << 16);
+        uint16_t* dst = ob.w2tb + (head * HID + threadIdx.x) * D + c0;
+        if constexpr (RW == 4) {
+          *(u32x2*)dst = u32x2{pk2[0], pk2[1]};
+        } else {
+          *(u32x4*)dst = u32x4{pk2[0], pk2[1], pk2[2], pk2[3]};
+        }
+      }
     }
   }
 }
