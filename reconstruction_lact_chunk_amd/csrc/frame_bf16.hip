@@ -42,7 +42,11 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
   const int nsl = h / kHidPerWg;
   const int64_t pairs = (int64_t)heads * plan.splits;
   const int upd_blocks = (int)(ceil_div(pairs, 8) * 8 * nsl);
-  const ApplyPlan ap = plan_apply(n_q, heads, kTargetWgs - upd_blocks);
+  ApplyPlan ap = plan_apply(n_q, heads, kTargetWgs - upd_blocks);
+  // With few compute units left over, the read's workgroups would get long
+  // runs and finish last: then they take the usual plan and queue behind
+  // the update's workgroups instead.
+  if (ap.chunk > 2 * plan.chunk) ap = plan_apply(n_q, heads);
   const unsigned blocks = (unsigned)(upd_blocks + (int64_t)heads * ap.splits);
 #define ZM_LAUNCH_FRAME(DD, HH)                                                                 \
   hipLaunchKernelGGL((k_frame_bf16<DD, HH>), dim3(blocks), dim3(512), 0, st, q, o, n_q, k, v,   \
