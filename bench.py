@@ -340,7 +340,7 @@ def main():
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
         if wide:
             for nm in ("update", "apply"):
-                kern[nm]["what"] = ("per 65,536-token block: hipBLASLt GEMMs (bf16, fp32 "
+                kern[nm]["what"] = ("per 131,072-token block: hipBLASLt GEMMs (bf16, fp32 "
                                     "accumulation) and the wide gate kernel")
         kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
         kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}

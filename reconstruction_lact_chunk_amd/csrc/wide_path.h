@@ -10,7 +10,7 @@ namespace zm {
 
 constexpr int kWideD = 1024;
 constexpr int kWideH = 2048;
-constexpr int64_t kWideBlock = 65536;               // tokens per block of the token buffers
+constexpr int64_t kWideBlock = 131072;              // tokens per block of the token buffers
 constexpr int kWideSub = 8;                         // partial slots: sub-blocks of each block
 constexpr size_t kWideLtWorkspace = (size_t)64 << 20;  // GEMM library workspace (= kLtWorkspace)
 

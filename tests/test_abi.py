@@ -109,7 +109,7 @@ def test_full_width_shape_workspace_and_limits():
     sets = 2 * 4 * welems * 2
     gemm_ws = 64 << 20
     assert base == sets + gemm_ws
-    blk = 65536
+    blk = 131072
     # token-block buffers (3 h bf16 per token, at most one block); 8 fp32
     # partial slots of 3 h d (one for fewer than 8 tokens)
     assert ws_size(de, 1000, 0)[1] == base + 1000 * 3 * 2048 * 2 + 8 * 3 * welems * 4
