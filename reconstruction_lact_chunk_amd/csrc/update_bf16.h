@@ -274,11 +274,6 @@ __device__ __forceinline__ void update_tiles(
     return Frag2{as_bf16x8(*(const u32x4*)(ktm + off)),
                  as_bf16x8(*(const u32x4*)(ktm + C::TILE + off))};
   };
-  auto fwd_mma = [&](Fwd& f, int mb, int ks, const Frag2& fr) {
-    f.a[mb] = mfma_bf16(fr.x, w1f[ks], f.a[mb]);
-    f.b[mb] = mfma_bf16(fr.x, w3f[ks], f.b[mb]);
-    f.e[mb] = mfma_bf16(fr.y, w2f[ks], f.e[mb]);
-  };
   auto bwd_frag = [&](int buf, int m) {  // K^T and V_eta^T column pieces
     const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
     const int col = 16 * m + 4 * (c & 3);
@@ -287,11 +282,6 @@ __device__ __forceinline__ void update_tiles(
                                          0, 1, 2, 3, 4, 5, 6, 7),
                  __builtin_shufflevector(lds_read_tr(ktm + C::TILE + oa),
                                          lds_read_tr(ktm + C::TILE + ob), 0, 1, 2, 3, 4, 5, 6, 7)};
-  };
-  auto bwd_mma = [&](int m, const Frag2& fr, const Grad& gr) {
-    acc1[m] = mfma_bf16(fr.x, gr.ga, acc1[m]);
-    acc3[m] = mfma_bf16(fr.x, gr.gb, acc3[m]);
-    acc2[m] = mfma_bf16(gr.u, fr.y, acc2[m]);
   };
 
   constexpr int NBS = MB;            // backward slots
