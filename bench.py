@@ -98,6 +98,16 @@ def make_events(torch, n):
     return evs
 
 
+def blas_name():
+    """The BLAS library NumPy was built against (name and version)."""
+    import numpy as np
+    try:
+        b = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:  # pragma: no cover
+        return "unknown BLAS"
+
+
 def cpu_baseline(inputs_host, sample_tokens, renorm, step_rule="gradient"):
     """The fp64 oracle (as it stands) on the first `sample_tokens` tokens."""
     import numpy as np
@@ -114,7 +124,7 @@ def cpu_baseline(inputs_host, sample_tokens, renorm, step_rule="gradient"):
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of the workload, all heads, update+apply "
-                      f"(n_q = n_kv = {sample_tokens}), NumPy fp64, {dt:.2f} s"}
+                      f"(n_q = n_kv = {sample_tokens}), NumPy fp64 ({blas_name()}), {dt:.2f} s"}
 
 
 def cpu_baseline_layer(xs, w_in, w_gate, gamma, w, sample_tokens, renorm, step_rule):
@@ -130,7 +140,8 @@ def cpu_baseline_layer(xs, w_in, w_gate, gamma, w, sample_tokens, renorm, step_r
     dt = time.perf_counter() - t0
     return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {sample_tokens} tokens of the workload through the whole layer "
-                      f"(projections, update + apply, output gate), NumPy fp64, {dt:.2f} s"}
+                      f"(projections, update + apply, output gate), NumPy fp64 ({blas_name()}), "
+                      f"{dt:.2f} s"}
 
 
 def main():
@@ -284,6 +295,21 @@ def main():
         graph_ms = g0.elapsed_time(g1) / K
         log(f"graph replay: {graph_ms:.4f} ms per step")
 
+    frame_ms = None
+    if wl.streaming and not wl.chunked:
+        # per-frame latency: events around every frame's call, in a pass after the timed region
+        w = [t.clone() for t in ws_layers[0]]
+        evs = []
+        for (s, e) in WL.frame_slices(wl):
+            a, b = make_events(torch, 2)
+            a.record(stream)
+            zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
+                           renorm=renorm, order=order, out=o[s:e], workspace=ws, step_rule=rule)
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        frame_ms = sorted(a.elapsed_time(b) for a, b in evs)
+
     stage_prof = None
     if not wl.streaming:  # the stage pass: every stage's events, outside the timed region
         stage_prof = [[make_events(torch, n_ev) for _ in ws_layers]
@@ -310,6 +336,13 @@ def main():
         frames = wl.frames
         result["value"] = n_tok / (ms / 1e3)
         result["per_frame_ms"] = ms / frames
+        if frame_ms:
+            med = float(np.median(frame_ms))
+            result["per_frame_latency_ms"] = {
+                "median": round(med, 4), "p99": round(float(np.percentile(frame_ms, 99)), 4),
+                "tokens_per_s_at_median": round(wl.tokens_per_frame / (med / 1e3)),
+                "how": "HIP events on the stream around each frame's call, in a separate pass "
+                       "after the timed region"}
     else:
         per_layer_ms = ms / wl.layers
         result["value"] = n_tok / (per_layer_ms / 1e3)
