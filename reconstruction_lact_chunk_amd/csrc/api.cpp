@@ -115,7 +115,9 @@ Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
     return L;
   }
   L.plan = plan_update(n_kv, d->heads, d->d_hidden);
-  L.total = L.part + round_up((size_t)L.plan.splits * 3 * welems * sizeof(float), 256);
+  // slots for any update of at most n_kv tokens (see update_slots)
+  const int slots = update_slots(n_kv, d->heads, d->d_hidden);
+  L.total = L.part + round_up((size_t)slots * 3 * welems * sizeof(float), 256);
   return L;
 }
 

@@ -119,6 +119,24 @@ inline UpdatePlan plan_update(int64_t n, int heads, int d_hidden) {
   return p;
 }
 
+// Partial-sum slots a workspace reserves for an update over n tokens: the
+// planned split count before rounding.  It never decreases with n and bounds
+// the realized count plan_update(n').splits of every n' <= n (that count is
+// ceil(n' / chunk') with chunk' >= n' / s', so at most s' <= s), which is what
+// lets one workspace, sized for the longest chunk, serve every shorter chunk.
+// The realized count alone is not monotonic: 1058 tokens over 16 heads of
+// hidden 256 realize 7 splits, 949 tokens 8.
+inline int update_slots(int64_t n, int heads, int d_hidden) {
+  if (n <= 0) return 0;
+  const int nsl = d_hidden / kHidPerWg > 0 ? d_hidden / kHidPerWg : 1;
+  int64_t target = kTargetWgs / (int64_t)(heads * nsl);
+  if (target < 1) target = 1;
+  int64_t s = ceil_div(ceil_div(n, kTok), kMinTilesPerChunk);
+  if (s > target) s = target;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
 struct ApplyPlan {
   int splits;
   int64_t chunk;

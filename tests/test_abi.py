@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 import torch
 
@@ -94,6 +95,25 @@ def test_bad_descriptor(field, value, expect):
     if field == "heads" and value > 0:
         de.ld_tok = value * de.d_head
     assert ws_size(de, 10, 10)[0] == expect
+
+
+def test_workspace_for_the_longest_chunk_covers_shorter_ones():
+    # zm_ttt_chunked sizes its workspace for the longest chunk; a shorter chunk
+    # can realize more split slots (16 heads, hidden 256: 1058 tokens -> 7,
+    # 949 tokens -> 8), so the size must cover the planned count
+    import test_tiling_host as TH
+    for heads, d, h in ((16, 64, 256), (8, 128, 256), (1, 128, 128), (3, 64, 256)):
+        de = desc(heads=heads, d=d, h=h)
+        slot = 3 * heads * h * d * 4
+        base = ws_size(de, 0, 0)[1]
+        rng = np.random.default_rng(heads * 1000 + d + h)
+        for longest in rng.integers(1, 40_000, 40):
+            need = max(TH.plan_update(int(m), heads, h)[0]
+                       for m in range(1, int(longest) + 1, max(1, int(longest) // 200)))
+            need = max(need, TH.plan_update(int(longest), heads, h)[0])
+            assert ws_size(de, int(longest), int(longest))[1] - base >= need * slot
+    de = desc(heads=16, d=64, h=256)
+    assert ws_size(de, 1058, 1058)[1] - ws_size(de, 0, 0)[1] >= 8 * 3 * 16 * 256 * 64 * 4
 
 
 @pytest.mark.parametrize("rule", [zm.STEP_GRADIENT, zm.STEP_NEWTON_SCHULZ])

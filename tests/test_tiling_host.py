@@ -36,6 +36,15 @@ def plan_update(n, heads, d_hidden):
     return ceil_div(n, chunk), chunk
 
 
+def update_slots(n, heads, d_hidden):
+    """Partial-sum slots the workspace reserves for n tokens (planned split count)."""
+    if n <= 0:
+        return 0
+    nsl = max(d_hidden // 128, 1)
+    target = max(TARGET_WGS // (heads * nsl), 1)
+    return min(max(ceil_div(ceil_div(n, TOK), MIN_TILES), 1), target)
+
+
 def plan_apply(n, heads):
     if n <= 0:
         return 0, 0
@@ -599,3 +608,28 @@ def test_newton_schulz_fragment_reads_conflict_free():
         for K in (64, 128):
             pitch = (K + pad) * el
             assert read_b128_degree([(l % 16) * pitch + (l // 16) * 16 for l in range(64)]) == 1
+
+
+@pytest.mark.parametrize("heads,d_hidden", [(1, 128), (1, 256), (3, 256), (8, 256), (16, 256),
+                                            (64, 128)])
+def test_reserved_slots_cover_every_shorter_update(heads, d_hidden):
+    """A multi-chunk call sizes its partial sums for the longest chunk, so the
+    reserved slot count must never decrease with n and must cover the realized
+    split count of every shorter chunk.  The realized count alone does not:
+    it drops and rises again (16 heads of hidden 256: 7 splits at 1058 tokens,
+    8 at 949)."""
+    realized_drops = False
+    best = 0
+    prev_slots = 0
+    for n in range(1, 70_000, 3):
+        splits = plan_update(n, heads, d_hidden)[0]
+        slots = update_slots(n, heads, d_hidden)
+        assert slots >= prev_slots
+        assert slots >= splits
+        best = max(best, splits)
+        assert slots >= best      # covers every n' <= n
+        realized_drops |= splits < best
+        prev_slots = slots
+    if (heads, d_hidden) == (16, 256):
+        assert realized_drops
+        assert plan_update(1058, 16, 256)[0] == 7 and plan_update(949, 16, 256)[0] == 8
