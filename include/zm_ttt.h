@@ -28,7 +28,8 @@
  *    call on a device (the GEMM library then holds its own resources until the
  *    process ends) and whose chosen algorithm per problem shape it caches.
  *  - Token tensors q, k, v, o: [n, heads, d_head] with a token stride of
- *    desc->ld_tok elements (ld_tok >= heads * d_head, multiple of 8).  Element
+ *    desc->ld_tok elements (heads * d_head <= ld_tok <= 2^24, multiple of 8;
+ *    a larger stride is rejected with ZM_ERR_INVALID_ARG).  Element
  *    type: bf16 or fp32 (desc->io_dtype).  Base pointers 16-byte aligned.
  *  - eta: fp32 [n, heads], contiguous (token-major), 4-byte aligned.
  *  - Weights: fp32, contiguous, 16-byte aligned; W1 and W3 [heads, h, d],

@@ -31,13 +31,14 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10101;  // 1.1.1
+constexpr int kVersion = 10102;  // 1.1.2
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
 constexpr int kMaxProfEvents = 14;
 // Widest layer (H d) whose output-gate rows a wave holds in registers.
 constexpr int64_t kMaxLayerWidth = 8192;
+constexpr int64_t kMaxLdTok = (int64_t)1 << 24;  // elements between token rows
 void* g_prof[kMaxProfEvents] = {};
 bool g_prof_on = false;
 
@@ -74,6 +75,8 @@ int check_desc(const zm_ttt_desc* d) {
   if (d->step_rule != ZM_STEP_GRADIENT && d->step_rule != ZM_STEP_NEWTON_SCHULZ)
     return ZM_ERR_INVALID_ARG;
   if (d->ld_tok < (int64_t)d->heads * d->d_head || d->ld_tok % 8 != 0) return ZM_ERR_INVALID_ARG;
+  // the bf16 kernels form a token's offset inside a 32-token tile in 32 bits
+  if (d->ld_tok > kMaxLdTok) return ZM_ERR_INVALID_ARG;
   if (d->heads > 64) return ZM_ERR_UNSUPPORTED;
   if (wide_shape(d->d_head, d->d_hidden)) {
     // full width: bf16 io only

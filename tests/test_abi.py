@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10101
+    assert zm.version() == 10102
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -88,6 +88,8 @@ def test_workspace_size_structure():
     ("step_rule", -1, zm.ERR_INVALID_ARG),
     ("ld_tok", 8 * 128 - 8, zm.ERR_INVALID_ARG),
     ("ld_tok", 8 * 128 + 4, zm.ERR_INVALID_ARG),
+    ("ld_tok", (1 << 24) + 8, zm.ERR_INVALID_ARG),   # 32-bit in-tile token offsets
+    ("ld_tok", 1 << 40, zm.ERR_INVALID_ARG),
 ])
 def test_bad_descriptor(field, value, expect):
     de = desc()
@@ -95,6 +97,10 @@ def test_bad_descriptor(field, value, expect):
     if field == "heads" and value > 0:
         de.ld_tok = value * de.d_head
     assert ws_size(de, 10, 10)[0] == expect
+
+
+def test_largest_token_stride_accepted():
+    assert ws_size(desc(ld=1 << 24), 10, 10)[0] == zm.OK
 
 
 def test_workspace_for_the_longest_chunk_covers_shorter_ones():
