@@ -118,7 +118,9 @@ typedef struct zm_ttt_desc {
 
 /* Bytes of workspace needed by any entry point below for an update over
  * n_kv tokens and an apply over n_q queries (either may be 0).  Writes the
- * size to *bytes.  Returns ZM_OK or a validation error. */
+ * size to *bytes.  Returns ZM_OK or a validation error.  The size never
+ * decreases as n_kv or n_q grows, so a workspace sized for (n_kv, n_q) also
+ * serves every call over at most n_kv tokens and n_q queries. */
 ZM_API int zm_ttt_workspace_size(const zm_ttt_desc* desc, int64_t n_kv, int64_t n_q, size_t* bytes);
 
 /* Update (review Eq. (2)-(3) and the renormalised update display):

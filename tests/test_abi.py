@@ -103,6 +103,23 @@ def test_largest_token_stride_accepted():
     assert ws_size(desc(ld=1 << 24), 10, 10)[0] == zm.OK
 
 
+@pytest.mark.parametrize("heads,d,h", [(16, 64, 256), (8, 128, 256), (3, 64, 128), (1, 1024, 2048)])
+def test_workspace_size_never_decreases(heads, d, h):
+    # the header promises that a workspace sized for (n_kv, n_q) serves every
+    # smaller call; a dense sweep, since the split plan is not monotonic in n
+    de = desc(heads=heads, d=d, h=h)
+    prev = 0
+    for n in list(range(0, 6000)) + [131_071, 131_072, 131_073, 500_000]:
+        st, size = ws_size(de, n, 0)
+        assert st == zm.OK and size >= prev, (n, size, prev)
+        prev = size
+    prev = 0
+    for n in (0, 1, 100, 131_072, 131_073, 400_000):
+        size = ws_size(de, 0, n)[1]
+        assert size >= prev
+        prev = size
+
+
 def test_workspace_for_the_longest_chunk_covers_shorter_ones():
     # zm_ttt_chunked sizes its workspace for the longest chunk; a shorter chunk
     # can realize more split slots (16 heads, hidden 256: 1058 tokens -> 7,
