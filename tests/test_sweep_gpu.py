@@ -130,3 +130,29 @@ def test_random_chunk_schedules_equal_separate_calls(seed):
         assert torch.equal(o, o_ref)
         for x, y in zip(state, ref):
             assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("heads,d,h", [(16, 64, 256), (8, 128, 256), (3, 128, 128)])
+def test_one_workspace_serves_every_smaller_call(heads, d, h):
+    """A workspace sized for the largest call, reused for smaller ones (the
+    order that once overflowed: 1058 tokens, then 949), gives bitwise the
+    results of calls with their own workspace."""
+    say(f"  case one workspace H={heads} d={d} h={h}")
+    sizes = [1058, 949, 1, 33, 1500, 700]
+    big = max(sizes)
+    w = WL.make_weights(heads, d, h, 5, "cuda")
+    desc = zm.binding.make_desc(*w, zm.BF16, True)
+    ws = torch.empty(zm.binding.workspace_size(desc, big, big), dtype=torch.uint8, device="cuda")
+    for i, n in enumerate(sizes):
+        q, k, v = tokens(n, heads, d, "bf16", 40 + i)
+        eta = WL.make_eta(n, heads, 40 + i, "cuda")
+        (a1, a2, a3), oa = zm.update_apply(k, v, eta, q, *w, renorm=True, workspace=ws)
+        (b1, b2, b3), ob = zm.update_apply(k, v, eta, q, *w, renorm=True)
+        sa = [x.clone() for x in w]
+        sb = [x.clone() for x in w]
+        pa = zm.stream_step(q, k, v, eta, *sa, renorm=True, workspace=ws)
+        pb = zm.stream_step(q, k, v, eta, *sb, renorm=True)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob) and torch.equal(pa, pb)
+        for x, y in zip((a1, a2, a3, *sa), (b1, b2, b3, *sb)):
+            assert torch.equal(x, y)
