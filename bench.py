@@ -24,6 +24,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -62,6 +64,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="also time the step captured once in a HIP graph and replayed (no host "
                         "launch overhead per call)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="with the default f700 workload, skip the other configurations (tiny, "
+                        "f8, f100 + target view, stream256, f700x24) timed after it")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a known-size "
                         "reference dispatch for scaling HBM counters)")
@@ -76,14 +81,17 @@ def source_hash(names):
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel, per_launch_units):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_f700.json")
-    if not os.path.exists(path):
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter record profiles/traffic_<kernel>_<workload>.json, if one
+    exists and was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if kernel not in KERNEL_SOURCES or not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
+    if rec.get("workload") != workload:
+        return None
     if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -142,6 +150,131 @@ def cpu_baseline_layer(xs, w_in, w_gate, gamma, w, sample_tokens, renorm, step_r
             "sample": f"first {sample_tokens} tokens of the workload through the whole layer "
                       f"(projections, update + apply, output gate), NumPy fp64 ({blas_name()}), "
                       f"{dt:.2f} s"}
+
+
+# Configurations reported beside the headline, each in its own timed region:
+# (name, timed steps, warm-up steps).  A stream256 step is 256 frames, an
+# f700x24 step 24 layers.
+EXTRA_CONFIGS = (("tiny", 200, 20), ("f8", 100, 10), ("f100", 30, 5), ("stream256", 3, 1),
+                 ("f700x24", 2, 1))
+
+
+def time_region(torch, stream, fn, steps, warmup):
+    """Average ms of fn() over `steps` calls after `warmup` untimed ones, from
+    HIP events on `stream` with the device synchronised on both sides."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def stage_ms(torch, zm, fn, steps=5):
+    """Average ms of the update partial sums (stage 1) and the apply (stage 3)
+    over `steps` calls of fn, from the library's events around each stage."""
+    evs = [make_events(torch, 8) for _ in range(steps)]
+    for ev in evs:
+        zm.set_profile_events(ev)
+        fn()
+    zm.set_profile_events(None)
+    torch.cuda.synchronize()
+    out = {}
+    for nm, s in (("update", 1), ("apply", 3)):
+        out[nm] = round(float(np.mean([ev[2 * s].elapsed_time(ev[2 * s + 1]) for ev in evs])), 4)
+    return out
+
+
+def run_configs(dev, torch, zm, WL, f700_inputs, seed):
+    """The other configurations of the benchmark, each timed in its own region
+    on the same stream: throughput, fraction of the bf16 matrix peak and, for
+    streaming, the per-frame latency."""
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, steps, warmup in EXTRA_CONFIGS:
+        wl = WL.WORKLOADS[name]
+        log(f"config {name}: {steps} timed steps after {warmup} warm-up")
+        if name == "f700x24":
+            x = f700_inputs
+        else:
+            x = WL.make_inputs(wl, seed=seed, device=dev)
+        io = zm.BF16 if wl.io_dtype == "bf16" else zm.F32
+        desc = zm.make_desc(x["w1"], x["w2"], x["w3"], io, wl.renorm, x["q"], x["k"])
+        p = wl.tokens_per_frame
+        ws = torch.empty(zm.workspace_size(desc, p, p) if wl.streaming else
+                         zm.workspace_size(desc, wl.n_kv, wl.n_q), dtype=torch.uint8, device=dev)
+        o = torch.empty_like(x["q"])
+        rec = {"workload": wl.description, "n_kv": wl.n_kv, "n_q": wl.n_q, "heads": wl.heads,
+               "d_head": wl.d_head, "d_hidden": wl.d_hidden, "io": wl.io_dtype,
+               "renorm": wl.renorm, "steps": steps, "warmup": warmup}
+        flops = wl.flops_per_token_update() * wl.n_kv + wl.flops_per_token_apply() * wl.n_q
+        if wl.streaming:
+            state = [t.clone() for t in (x["w1"], x["w2"], x["w3"])]
+            frames = WL.frame_slices(wl)
+
+            def frame(s, e):
+                zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *state,
+                               renorm=wl.renorm, order=zm.APPLY_THEN_UPDATE, out=o[s:e],
+                               workspace=ws)
+
+            def fn():
+                for (s, e) in frames:
+                    frame(s, e)
+            ms = time_region(torch, stream, fn, steps, warmup)
+            lat = []
+            for (s, e) in frames:
+                a, b = make_events(torch, 2)
+                a.record(stream)
+                frame(s, e)
+                b.record(stream)
+                lat.append((a, b))
+            torch.cuda.synchronize()
+            lat = [a.elapsed_time(b) for a, b in lat]
+            med = float(np.median(lat))
+            rec.update({"order": "apply_then_update", "ms_per_step": round(ms, 4),
+                        "per_frame_ms": round(ms / wl.frames, 5),
+                        "tokens_per_s": round(wl.n_kv / (ms / 1e3)),
+                        "per_frame_latency_ms": {
+                            "median": round(med, 4), "p99": round(float(np.percentile(lat, 99)), 4),
+                            "tokens_per_s_at_median": round(p / (med / 1e3)),
+                            "how": "HIP events around each frame's call, in a pass after the "
+                                   "timed region"},
+                        "frac_bf16_peak": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        else:
+            if wl.layers > 1:
+                wsets = [WL.make_weights(wl.heads, wl.d_head, wl.d_hidden, seed, dev, layer=i)
+                         for i in range(wl.layers)]
+            else:
+                wsets = [(x["w1"], x["w2"], x["w3"])]
+            w_out = [tuple(torch.empty_like(w) for w in ws3) for ws3 in wsets]
+
+            def one(li):
+                zm.update_apply(x["k"], x["v"], x["eta"], x["q"], *wsets[li], renorm=wl.renorm,
+                                w_out=w_out[li], out=o, workspace=ws)
+
+            def fn():
+                for li in range(len(wsets)):
+                    one(li)
+            ms = time_region(torch, stream, fn, steps, warmup)
+            per_layer = ms / wl.layers
+            rec.update({"ms_per_step": round(ms, 4), "per_layer_ms": round(per_layer, 4),
+                        "tokens_per_s": round(wl.n_kv / (per_layer / 1e3)),
+                        "frac_bf16_peak": round(flops / (per_layer / 1e3) / 1e12
+                                                / PEAK_BF16_TFLOPS, 4),
+                        "kernels_ms": stage_ms(torch, zm, lambda: one(0))})
+            if name == "f100":
+                rec["target_view_queries"] = wl.extra_queries
+            del wsets, w_out
+        out[name] = rec
+        del ws, o
+        if name != "f700x24":
+            del x
+    return out
 
 
 def main():
@@ -414,7 +547,7 @@ def main():
             "kernel": kname,
             "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-            "traffic": None if wide else stored_traffic(dom, n_tok),
+            "traffic": None if wide else stored_traffic(dom, wl.name),
         }
         result["kernels"] = kern
         result["kernels_timing"] = (f"{dom}: HIP events around it in every timed step; other "
@@ -448,6 +581,9 @@ def main():
         result["graph_ms_per_step"] = round(graph_ms, 4)
         result["graph_value"] = (n_tok / (graph_ms / wl.layers / 1e3) if not wl.streaming
                                  else n_tok / (graph_ms / 1e3))
+
+    if wl.name == "f700" and not args.no_configs and rule == zm.STEP_GRADIENT and renorm:
+        result["configs"] = run_configs(dev, torch, zm, WL, x, args.seed)
 
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens

@@ -134,40 +134,74 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_weights(w1, w2, w3):
+def _check_weights(w1, w2, w3, device=True):
     for w in (w1, w2, w3):
         if w.dtype != torch.float32 or not w.is_contiguous() or w.dim() != 3:
             raise ZmError("weights must be contiguous fp32 [heads, h, d] / [heads, d, h]")
-        if not w.is_cuda:
-            raise ZmError("weights must be on the GPU")
     heads, h, d = w1.shape
     if w3.shape != w1.shape or tuple(w2.shape) != (heads, d, h):
         raise ZmError("weight shapes disagree: W1, W3 [H, h, d]; W2 [H, d, h]")
+    if device:
+        _on_gpu(w1, w2, w3, what="weights")
     return heads, d, h
 
 
-def _token_ld(x, heads, d, io):
+def _on_gpu(*tensors, what="tensors"):
+    """Device check, made after the shape checks so that a shape error is
+    reported as such whatever the tensors' device."""
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ZmError(f"{what} must be on the GPU")
+
+
+def _token_ld(x, heads, d, io, rows=None, name="token tensor"):
+    """Checks one token tensor whatever its length (dtype, [n, H, d] shape,
+    inner strides, row count when `rows` is given, device) and returns its token
+    stride, or None when it has at most one row (no stride to agree on)."""
     if x is None:
         return None
     if x.dtype not in _IO or _IO[x.dtype] != io:
-        raise ZmError("token tensors must all share the io dtype (bf16 or fp32)")
+        raise ZmError(f"{name}: token tensors must all share the io dtype (bf16 or fp32)")
     if x.dim() != 3 or x.shape[1] != heads or x.shape[2] != d:
-        raise ZmError(f"token tensor shape {tuple(x.shape)} != [n, {heads}, {d}]")
+        raise ZmError(f"{name}: shape {tuple(x.shape)} != [n, {heads}, {d}]")
+    if rows is not None and x.shape[0] != rows:
+        raise ZmError(f"{name}: {x.shape[0]} rows, the call needs {rows}")
     if x.shape[0] > 0 and (x.stride(2) != 1 or x.stride(1) != d):
-        raise ZmError("token tensors need unit stride on d and d on heads")
-    if not x.is_cuda:
-        raise ZmError("token tensors must be on the GPU")
-    return x.stride(0) if x.shape[0] > 1 else heads * d
+        raise ZmError(f"{name}: token tensors need unit stride on d and d on heads")
+    return x.stride(0) if x.shape[0] > 1 else None
 
 
-def make_desc(w1, w2, w3, io_dtype: int, renorm: bool, *tokens, step_rule: int = STEP_GRADIENT
-              ) -> Desc:
-    heads, d, h = _check_weights(w1, w2, w3)
-    lds = {_token_ld(x, heads, d, io_dtype) for x in tokens if x is not None and x.shape[0] > 1}
+def make_desc(w1, w2, w3, io_dtype: int, renorm: bool, *tokens, step_rule: int = STEP_GRADIENT,
+              rows=None, check_device=True) -> Desc:
+    """Descriptor of a call on the weights w1..w3 and the token tensors
+    `tokens`; every token tensor is checked, and `rows` (one entry per token
+    tensor, None to skip) gives the row count each must have.  With
+    check_device=False the caller checks the devices itself, last."""
+    heads, d, h = _check_weights(w1, w2, w3, device=False)
+    rows = rows if rows is not None else [None] * len(tokens)
+    lds = set()
+    for i, (x, r) in enumerate(zip(tokens, rows)):
+        ld = _token_ld(x, heads, d, io_dtype, r, f"token tensor {i}")
+        if ld is not None:
+            lds.add(ld)
     if len(lds) > 1:
         raise ZmError("all token tensors of one call must share the token stride")
+    if check_device:
+        _on_gpu(w1, w2, w3, what="weights")
+        _on_gpu(*tokens, what="token tensors")
     ld = lds.pop() if lds else heads * d
     return Desc(heads, d, h, io_dtype, RENORM_ROW if renorm else RENORM_NONE, int(step_rule), ld)
+
+
+def _check_out_weights(outs, w1, w2, w3):
+    """Output weights: fp32, contiguous and of the input weights' shapes (their
+    device is checked with the call's other tensors)."""
+    if len(outs) != 3:
+        raise ZmError("need three output weight tensors (W1, W2, W3)")
+    for o, w, nm in zip(outs, (w1, w2, w3), ("W1", "W2", "W3")):
+        if tuple(o.shape) != tuple(w.shape):
+            raise ZmError(f"output {nm} has shape {tuple(o.shape)}, the weights {tuple(w.shape)}")
+    _check_weights(*outs, device=False)
 
 
 def _io_of(*tokens) -> int:
@@ -182,8 +216,6 @@ def _io_of(*tokens) -> int:
 def _eta(eta, n, heads):
     if eta.dtype != torch.float32 or not eta.is_contiguous() or tuple(eta.shape) != (n, heads):
         raise ZmError(f"eta must be contiguous fp32 [{n}, {heads}]")
-    if not eta.is_cuda:
-        raise ZmError("eta must be on the GPU")
 
 
 def _like_tokens(x):
@@ -223,13 +255,13 @@ def update(k, v, eta, w1, w2, w3, renorm=False, out=None, workspace=None,
     """W_hat = step(W; k, v, eta) (+ row renorm).  Returns (W1_hat, W2_hat, W3_hat);
     pass out=(w1, w2, w3) to update in place."""
     io = _io_of(k, v)
-    desc = make_desc(w1, w2, w3, io, renorm, k, v, step_rule=step_rule)
     n = k.shape[0]
-    if v.shape[0] != n:
-        raise ZmError("k and v token counts differ")
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, step_rule=step_rule, rows=[n, n],
+                     check_device=False)
     _eta(eta, n, desc.heads)
     outs = out if out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
-    _check_weights(*outs)
+    _check_out_weights(outs, w1, w2, w3)
+    _on_gpu(k, v, eta, w1, w2, w3, *outs)
     ws, _ = _workspace(desc, n, 0, w1.device, workspace)
     st = load_library().zm_ttt_update(ctypes.byref(desc), n, _ptr(k), _ptr(v), _ptr(eta),
                                       _ptr(w1), _ptr(w2), _ptr(w3), *map(_ptr, outs), _ptr(ws),
@@ -242,8 +274,8 @@ def apply(q, w1, w2, w3, out=None, workspace=None):
     """o = f_W(q) per head; q [n, H, d] -> o [n, H, d] (same dtype)."""
     io = _io_of(q)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, False, q, o)
     n = q.shape[0]
+    desc = make_desc(w1, w2, w3, io, False, q, o, rows=[n, n])  # checks every device
     ws, _ = _workspace(desc, 0, n, w1.device, workspace)
     st = load_library().zm_ttt_apply(ctypes.byref(desc), n, _ptr(q), _ptr(w1), _ptr(w2),
                                      _ptr(w3), _ptr(o), _ptr(ws), _ws_bytes(ws),
@@ -258,13 +290,13 @@ def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, w
     Returns ((W1_hat, W2_hat, W3_hat), o)."""
     io = _io_of(k, v, q)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o, step_rule=step_rule)
     n_kv, n_q = k.shape[0], q.shape[0]
-    if v.shape[0] != n_kv:
-        raise ZmError("k and v token counts differ")
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o, step_rule=step_rule,
+                     rows=[n_kv, n_kv, n_q, n_q], check_device=False)
     _eta(eta, n_kv, desc.heads)
     outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
-    _check_weights(*outs)
+    _check_out_weights(outs, w1, w2, w3)
+    _on_gpu(k, v, eta, q, o, w1, w2, w3, *outs)
     ws, _ = _workspace(desc, n_kv, n_q, w1.device, workspace)
     st = load_library().zm_ttt_update_apply(
         ctypes.byref(desc), n_kv, _ptr(k), _ptr(v), _ptr(eta), n_q, _ptr(q), _ptr(w1), _ptr(w2),
@@ -279,11 +311,11 @@ def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE,
     Returns o (read with W(t-1) for APPLY_THEN_UPDATE, W(t) otherwise)."""
     io = _io_of(q, k, v)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule)
     n = q.shape[0]
-    if k.shape[0] != n or v.shape[0] != n:
-        raise ZmError("q, k and v of one frame must have the same token count")
+    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule, rows=[n] * 4,
+                     check_device=False)
     _eta(eta, n, desc.heads)
+    _on_gpu(q, k, v, o, eta, w1, w2, w3)
     ws, _ = _workspace(desc, n, n, w1.device, workspace)
     st = load_library().zm_ttt_stream_step(ctypes.byref(desc), int(order), n, _ptr(q), _ptr(k),
                                            _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2), _ptr(w3),
@@ -299,15 +331,15 @@ def chunked(q, k, v, eta, offsets, w1, w2, w3, renorm=False, order=UPDATE_THEN_A
     sequence of n_chunks booleans (False: read only).  Returns o."""
     io = _io_of(q, k, v)
     o = out if out is not None else _like_tokens(q)
-    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule)
     offs = [int(x) for x in offsets]
     n_chunks = len(offs) - 1
     if n_chunks < 0:
         raise ZmError("offsets needs at least one entry")
     n = offs[-1]
-    if q.shape[0] != n or k.shape[0] != n or v.shape[0] != n:
-        raise ZmError(f"q, k, v must hold offsets[-1] = {n} tokens")
+    desc = make_desc(w1, w2, w3, io, renorm, q, k, v, o, step_rule=step_rule, rows=[n] * 4,
+                     check_device=False)
     _eta(eta, n, desc.heads)
+    _on_gpu(q, k, v, o, eta, w1, w2, w3)
     longest = max([b - a for a, b in zip(offs, offs[1:])] + [0])
     ws, _ = _workspace(desc, longest, longest, w1.device, workspace)
     off_arr = (ctypes.c_int64 * len(offs))(*offs)
@@ -347,10 +379,9 @@ def layer(x, w_in, w_gate, gamma, w1, w2, w3, eta_scale=0.01, rms_eps=1e-6, reno
     """The whole layer on one chunk: projections of x [n, d_in] (bf16) to q, k,
     v and the rate, update, apply, output gate.  Returns ((W1_hat, W2_hat,
     W3_hat), o [n, H d] bf16)."""
-    heads, d, h = _check_weights(w1, w2, w3)
-    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_cuda or (x.shape[0] > 1 and
-                                                                       x.stride(1) != 1):
-        raise ZmError("x must be a 2-D bf16 GPU tensor with unit column stride")
+    heads, d, h = _check_weights(w1, w2, w3, device=False)
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or (x.shape[0] > 0 and x.stride(1) != 1):
+        raise ZmError("x must be a 2-D bf16 tensor with unit column stride")
     n = x.shape[0]
     if tuple(w_in.shape) != (3 * heads * d + heads, x.shape[1]):
         raise ZmError(f"w_in must be [{3 * heads * d + heads}, {x.shape[1]}]")
@@ -358,14 +389,19 @@ def layer(x, w_in, w_gate, gamma, w1, w2, w3, eta_scale=0.01, rms_eps=1e-6, reno
         raise ZmError("w_gate must be [H d, H d] and gamma [H d]")
     o = out if out is not None else torch.empty((n, heads * d), dtype=torch.bfloat16,
                                                 device=x.device)
+    if o.dtype != torch.bfloat16 or o.dim() != 2 or tuple(o.shape) != (n, heads * d):
+        raise ZmError(f"out must be bf16 [{n}, {heads * d}], got {o.dtype} {tuple(o.shape)}")
+    if n > 0 and o.stride(1) != 1:
+        raise ZmError("out needs unit column stride")
+    outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_out_weights(outs, w1, w2, w3)
+    _on_gpu(x, w1, w2, w3, w_in, w_gate, gamma, o, *outs, what="the layer's tensors")
     desc = Desc(heads, d, h, BF16, RENORM_ROW if renorm else RENORM_NONE, int(step_rule),
                 o.stride(0) if n > 1 else heads * d)
     lw = make_layer_weights(w_in, w_gate, gamma, eta_scale, rms_eps)
     need = layer_workspace_size(desc, lw, n)
     ws = workspace if workspace is not None else torch.empty(max(need, 256), dtype=torch.uint8,
                                                              device=x.device)
-    outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
-    _check_weights(*outs)
     st = load_library().zm_ttt_layer(
         ctypes.byref(desc), ctypes.byref(lw), n, _ptr(x), x.stride(0) if n > 1 else x.shape[1],
         _ptr(w1), _ptr(w2), _ptr(w3), *map(_ptr, outs), _ptr(o), _ptr(ws), _ws_bytes(ws),

@@ -30,6 +30,10 @@ COMMON = [
 ]
 # Packed fp32 VALU forms are kept out of the generated code.
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Address and undefined-behaviour sanitizers for the host half only (argument
+# validation, workspace carving, launch set-up); device code is built as usual.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address,undefined",
+                 "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 
 
 def hipcc() -> str:
@@ -39,10 +43,11 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool, defines=(), build_dir=BUILD) -> str:
+def _compile(src: str, verbose: bool, defines=(), build_dir=BUILD, extra=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
     defs = [f"-D{d}" for d in defines]
-    cmd = [hipcc(), *COMMON, *defs, *DEVICE, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *defs, *DEVICE, *extra, "-x", "hip", "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,14 +58,19 @@ def _compile(src: str, verbose: bool, defines=(), build_dir=BUILD) -> str:
     return obj
 
 
-def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+def build(verbose: bool = False, defines=(), out: str = LIB, host_sanitize: bool = False) -> str:
     """Compile every source and link the library (default: libzmttt.so next
     to this file); `defines` are extra preprocessor definitions such as tuning
-    switches.  Returns the library path."""
+    switches.  host_sanitize instruments the host code with ASan and UBSan (the
+    resulting library needs the sanitizer runtime preloaded; see
+    sanitizer_runtime()).  Returns the library path."""
+    if host_sanitize and out == LIB:
+        raise ValueError("a sanitized build goes to its own path, not over the product library")
     build_dir = BUILD if out == LIB else out + ".objs"
     os.makedirs(build_dir, exist_ok=True)
+    extra = HOST_SANITIZE if host_sanitize else ()
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir, extra), SOURCES))
     tmp = out + ".tmp"
     rocm_lib = os.path.join(os.path.dirname(os.path.dirname(os.path.realpath(hipcc()))), "lib")
     # hipBLASLt serves the plain GEMMs of the full-width head shape
@@ -73,6 +83,19 @@ def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, out)
     return out
+
+
+def sanitizer_runtime() -> str:
+    """Path of the compiler's shared ASan runtime (it carries the UBSan
+    handlers too), to be preloaded into a process that loads a sanitized
+    build."""
+    res = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "llvm",
+                                       "bin", "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("shared ASan runtime not found")
+    return path
 
 
 if __name__ == "__main__":

@@ -129,6 +129,30 @@ WSet carve_set(void* ws, size_t off, size_t welems) {
   return WSet{p, p + welems, p + 2 * welems, p + 3 * welems};
 }
 
+// Host-side bound of the partial-sum slots a launch is about to write:
+// `splits` slots of 3 h d fp32 per head from byte offset part_off.  The
+// workspace size check at entry already covers every planned count; this
+// check turns a planner slip into a status code instead of a write past the
+// caller's allocation.
+int check_part_range(size_t part_off, int splits, size_t welems, size_t ws_bytes) {
+  const size_t need = part_off + (size_t)splits * 3 * welems * sizeof(float);
+  if (splits < 0 || need > ws_bytes) {
+    set_last_error("partial sums of %d slots need %zu workspace bytes, %zu given", splits, need,
+                   ws_bytes);
+    return ZM_ERR_WORKSPACE;
+  }
+  return ZM_OK;
+}
+
+int check_wide_bufs(const WideBufs& wb, size_t ws_bytes) {
+  if (!wb.fits) {
+    set_last_error("full-width token-block buffers and partial sums exceed the %zu-byte workspace",
+                   ws_bytes);
+    return ZM_ERR_WORKSPACE;
+  }
+  return ZM_OK;
+}
+
 int check_counts(int64_t n_kv, int64_t n_q) {
   const int64_t kMax = (int64_t)1 << 31;  // token indices fit 32-bit tile counts
   if (n_kv < 0 || n_q < 0 || n_kv > kMax || n_q > kMax) return ZM_ERR_INVALID_ARG;
@@ -192,7 +216,9 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
   const WSet a = carve_set(ws, L.set_a, welems);
   if (is_wide(d)) {
     const bool ns = d->step_rule == ZM_STEP_NEWTON_SCHULZ;
-    const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n, ns);
+    const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n, 0,
+                                  ns);
+    ZM_TRY(check_wide_bufs(wb, wsp.bytes));
     int splits = L.plan.splits;
     if (n > 0) {
       if (!cast_done) {
@@ -216,6 +242,7 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
     return ZM_OK;
   }
   float* part = (float*)((char*)ws + L.part);
+  ZM_TRY(check_part_range(L.part, L.plan.splits, welems, wsp.bytes));
   if (n > 0) {
     if (d->io_dtype == ZM_BF16) {
       if (!cast_done) {
@@ -262,7 +289,8 @@ int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const flo
   if (is_wide(d)) {
     const Layout L = layout(d, 0, n);
     const WideBufs wb = wide_bufs(wsp.p, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, 0,
-                                  d->step_rule == ZM_STEP_NEWTON_SCHULZ);
+                                  n, d->step_rule == ZM_STEP_NEWTON_SCHULZ);
+    ZM_TRY(check_wide_bufs(wb, wsp.bytes));
     return wide_apply(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)q,
                       (uint16_t*)o, set, wb, st);
   }
@@ -300,6 +328,7 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
       // The read and the first update's partial sums use only the incoming W:
       // one launch for both (both stages' profile events bracket it).
       float* part = (float*)((char*)ws.p + L.part);
+      ZM_TRY(check_part_range(L.part, L.plan.splits, welems, ws.bytes));
       {
         Scoped su(kStageUpdate, st);
         Scoped sa(kStageApply, st);
@@ -353,6 +382,7 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
   // with chunk rc's read in the same launch when rc >= 0.
   auto step = [&](int64_t c, int64_t rc) -> int {
     const UpdatePlan plan = plan_update(len(c), hd, hh);
+    ZM_TRY(check_part_range(L0.part, plan.splits, (size_t)hd * hh * dh, ws.bytes));
     const float* e = eta + offsets[c] * hd;
     {
       Scoped su(kStageUpdate, st);

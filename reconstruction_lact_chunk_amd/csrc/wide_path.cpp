@@ -65,7 +65,7 @@ size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool
 }
 
 WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
-                   bool ns) {
+                   int64_t n_q, bool ns) {
   WideBufs w;
   char* p = (char*)ws + base;
   w.lt_ws = p;
@@ -76,7 +76,13 @@ WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int
   const size_t part = (size_t)wide_splits(n_kv) * heads * 3 * (size_t)h * d * sizeof(float);
   // partial sums at the end of the workspace, so the token-block buffers can
   // be sized by the larger of the update and apply counts
-  w.part = (float*)((char*)ws + ((ws_bytes - part) / 256) * 256);
+  const size_t part_off = part <= ws_bytes ? ((ws_bytes - part) / 256) * 256 : 0;
+  w.part = (float*)((char*)ws + part_off);
+  const int64_t rows_kv = n_kv < kWideBlock ? n_kv : kWideBlock;
+  const int64_t rows_q = n_q < kWideBlock ? n_q : kWideBlock;
+  const int64_t rows = rows_kv > rows_q ? rows_kv : rows_q;
+  const size_t ab_end = base + kWideLtWorkspace + ns_bytes + (size_t)rows * 3 * h * sizeof(uint16_t);
+  w.fits = part <= ws_bytes && ab_end <= part_off;
   return w;
 }
 

@@ -20,6 +20,7 @@ struct WideBufs {
   void* ns;           // Newton-Schulz buffers (with that step rule), else null
   uint16_t* ab;       // token-block buffers: [rows][2 h] then [rows][h], bf16
   float* part;        // partial sums [kWideSub][heads][3][h d], at the end of the workspace
+  bool fits;          // every buffer above lies inside the workspace, block buffers below part
 };
 
 bool wide_shape(int d, int h);
@@ -27,8 +28,11 @@ int64_t wide_splits(int64_t n_kv);
 // Workspace bytes beyond the two bf16 weight sets (ns: with the Newton-Schulz
 // step rule).
 size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool ns);
+// The buffers of a call with an update over n_kv tokens and an apply over n_q
+// queries (either may be 0) inside the caller's workspace of ws_bytes; `fits`
+// says whether they all lie inside it (checked on the host before any launch).
 WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
-                   bool ns);
+                   int64_t n_q, bool ns);
 
 // Newton-Schulz of every matrix of the summed partials part0 ([heads][3][h d]),
 // in place; ns_ws holds wide_ns_bytes().

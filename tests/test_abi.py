@@ -331,3 +331,91 @@ def test_binding_rejects_host_tensors_and_bad_shapes():
         zm.make_desc(w1, w2.transpose(1, 2), w3, zm.F32, False)
     with pytest.raises(zm.ZmError):
         zm.make_desc(w1.double(), w2, w3, zm.F32, False)
+
+
+def _host_case(n=10, heads=2, d=64, h=128, dtype=torch.float32):
+    w1, w3 = torch.zeros(heads, h, d), torch.zeros(heads, h, d)
+    w2 = torch.zeros(heads, d, h)
+    tok = lambda m: torch.zeros(m, heads, d, dtype=dtype)  # noqa: E731
+    return w1, w2, w3, tok, torch.zeros(n, heads)
+
+
+def test_binding_checks_every_token_tensor_whatever_its_length():
+    # Shape, dtype and stride errors are reported before the device check, so
+    # host tensors reach them here; nothing is launched.
+    w1, w2, w3, tok, eta = _host_case()
+    with pytest.raises(zm.ZmError, match="io dtype"):      # one query row of the wrong dtype
+        zm.update_apply(tok(10), tok(10), eta, tok(1).to(torch.bfloat16), w1, w2, w3)
+    with pytest.raises(zm.ZmError, match=r"shape \(1, 3, 64\)"):
+        zm.update_apply(tok(10), tok(10), eta, torch.zeros(1, 3, 64), w1, w2, w3)
+    bad_stride = torch.zeros(1, 64, 2).transpose(1, 2)     # [1, 2, 64], d not unit-stride
+    with pytest.raises(zm.ZmError, match="unit stride"):
+        zm.apply(bad_stride, w1, w2, w3)
+    with pytest.raises(zm.ZmError, match="unit stride"):
+        zm.update(bad_stride, tok(1), torch.zeros(1, 2), w1, w2, w3)
+    with pytest.raises(zm.ZmError, match="on the GPU"):    # well-formed host tensors
+        zm.update_apply(tok(10), tok(10), eta, tok(1), w1, w2, w3)
+
+
+def test_binding_checks_output_rows_and_weight_shapes():
+    w1, w2, w3, tok, eta = _host_case()
+    with pytest.raises(zm.ZmError, match="9 rows"):
+        zm.apply(tok(10), w1, w2, w3, out=tok(9))
+    with pytest.raises(zm.ZmError, match="11 rows"):
+        zm.update_apply(tok(10), tok(10), eta, tok(10), w1, w2, w3, out=tok(11))
+    with pytest.raises(zm.ZmError, match="1 rows"):        # a one-row output for ten queries
+        zm.stream_step(tok(10), tok(10), tok(10), eta, w1, w2, w3, out=tok(1))
+    with pytest.raises(zm.ZmError, match="10 rows, the call needs 9"):  # v longer than k
+        zm.update(tok(9), tok(10), eta, w1, w2, w3)
+    with pytest.raises(zm.ZmError, match="5 rows"):
+        zm.chunked(tok(10), tok(10), tok(10), eta, [0, 4, 10], w1, w2, w3, out=tok(5))
+    small = (torch.zeros(2, 64, 64), w2.clone(), w3.clone())
+    with pytest.raises(zm.ZmError, match="output W1"):
+        zm.update(tok(10), tok(10), eta, w1, w2, w3, out=small)
+    with pytest.raises(zm.ZmError, match="output W2"):
+        zm.update_apply(tok(10), tok(10), eta, tok(10), w1, w2, w3,
+                        w_out=(w1.clone(), torch.zeros(2, 64, 64), w3.clone()))
+
+
+def test_binding_checks_the_layer_output():
+    heads, d, h, d_in, n = 2, 64, 128, 64, 6
+    w1, w3 = torch.zeros(heads, h, d), torch.zeros(heads, h, d)
+    w2 = torch.zeros(heads, d, h)
+    x = torch.zeros(n, d_in, dtype=torch.bfloat16)
+    w_in = torch.zeros(3 * heads * d + heads, d_in, dtype=torch.bfloat16)
+    w_gate = torch.zeros(heads * d, heads * d, dtype=torch.bfloat16)
+    gamma = torch.ones(heads * d)
+    with pytest.raises(zm.ZmError, match="out must be bf16"):
+        zm.layer(x, w_in, w_gate, gamma, w1, w2, w3, out=torch.zeros(n - 1, heads * d,
+                                                                      dtype=torch.bfloat16))
+    with pytest.raises(zm.ZmError, match="out must be bf16"):
+        zm.layer(x, w_in, w_gate, gamma, w1, w2, w3, out=torch.zeros(n, heads * d))
+    with pytest.raises(zm.ZmError, match="output W3"):
+        zm.layer(x, w_in, w_gate, gamma, w1, w2, w3,
+                 w_out=(w1.clone(), w2.clone(), torch.zeros(heads, h, d + 8)))
+    with pytest.raises(zm.ZmError, match="on the GPU"):
+        zm.layer(x, w_in, w_gate, gamma, w1, w2, w3)
+
+
+def test_undersized_workspaces_are_rejected_before_any_launch():
+    # the sequence that once overran the partial sums: a 1058-token chunk
+    # followed by a 949-token one (16 heads, hidden 256: 7 then 8 splits); a
+    # workspace with fewer slots than the longest chunk plans is refused
+    offs = [0, 1058, 2007]
+    for (heads, d, h), longest in (((16, 64, 256), 500), ((16, 64, 256), 700),
+                                   ((8, 128, 256), 949), ((8, 128, 256), 1000)):
+        de = desc(heads=heads, d=d, h=h)
+        assert ws_size(de, longest, longest)[1] < ws_size(de, 1058, 1058)[1]
+        assert call_chunked(de, offs, ws_bytes=ws_size(de, longest, longest)[1]) == \
+            zm.ERR_WORKSPACE, (heads, longest)
+    # the full-width head: token-block buffers hold min(n, 131072) rows of 3 h
+    wd = desc(heads=1, d=1024, h=2048)
+    L = lib()
+    for n_kv, n_q, sized_for in ((131_072, 0, (131_071, 0)), (1000, 200_000, (1000, 1000)),
+                                 (200_000, 10, (131_000, 10)), (8, 0, (7, 0))):
+        need = ws_size(wd, *sized_for)[1]
+        st = L.zm_ttt_update_apply(ctypes.byref(wd), n_kv, GOOD, GOOD, GOOD, n_q, GOOD, GOOD,
+                                   GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, need, None)
+        assert st == zm.ERR_WORKSPACE, (n_kv, n_q)
+    assert L.zm_ttt_apply(ctypes.byref(wd), 131_073, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
+                          ws_size(wd, 0, 100_000)[1], None) == zm.ERR_WORKSPACE

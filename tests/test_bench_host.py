@@ -22,17 +22,28 @@ def test_more_than_one_gpu_exits_with_a_message():
     assert r.stdout == ""
 
 
-def test_stored_traffic_follows_the_kernel_source_hash(monkeypatch):
-    n = WL.WORKLOADS["f700"].n_kv
+def test_stored_traffic_follows_the_kernel_source_hash_and_workload(monkeypatch):
     with open(os.path.join(ROOT, "profiles", "traffic_update_f700.json")) as f:
         rec = json.load(f)
+    assert rec["workload"] == "f700"
     live = bench.source_hash(bench.KERNEL_SOURCES["update"])
     if rec["source_sha256_16"] == live:
-        assert bench.stored_traffic("update", n) == rec["hbm_bytes_per_launch"]
+        assert bench.stored_traffic("update", "f700") == rec["hbm_bytes_per_launch"]
+    # another workload's launch moves other bytes: no record, no figure
+    for other in ("f8", "f100", "tiny", "stream256"):
+        if not os.path.exists(os.path.join(ROOT, "profiles", f"traffic_update_{other}.json")):
+            assert bench.stored_traffic("update", other) is None
     # a source that differs from the one the counters were taken on gives no figure
     monkeypatch.setattr(bench, "source_hash", lambda names: "0" * 16)
-    assert bench.stored_traffic("update", n) is None
-    assert bench.stored_traffic("no_such_kernel", n) is None
+    assert bench.stored_traffic("update", "f700") is None
+    assert bench.stored_traffic("no_such_kernel", "f700") is None
+
+
+def test_extra_configs_cover_every_configuration():
+    names = [c[0] for c in bench.EXTRA_CONFIGS]
+    assert set(names) == {"tiny", "f8", "f100", "stream256", "f700x24"}
+    for name, steps, warmup in bench.EXTRA_CONFIGS:
+        assert name in WL.WORKLOADS and steps >= 1 and warmup >= 1
 
 
 def test_source_hash_covers_every_listed_file():
