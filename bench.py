@@ -217,26 +217,29 @@ def run_configs(dev, torch, zm, WL, f700_inputs, seed):
             state = [t.clone() for t in (x["w1"], x["w2"], x["w3"])]
             frames = WL.frame_slices(wl)
 
-            def frame(s, e):
+            def frame(s, e, reuse):
                 zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *state,
                                renorm=wl.renorm, order=zm.APPLY_THEN_UPDATE, out=o[s:e],
-                               workspace=ws)
+                               workspace=ws, emit_bf16=True, reuse_bf16=reuse)
 
             def fn():
-                for (s, e) in frames:
-                    frame(s, e)
+                for i, (s, e) in enumerate(frames):
+                    frame(s, e, i > 0)
             ms = time_region(torch, stream, fn, steps, warmup)
             lat = []
-            for (s, e) in frames:
+            for i, (s, e) in enumerate(frames):
                 a, b = make_events(torch, 2)
                 a.record(stream)
-                frame(s, e)
+                frame(s, e, i > 0)
                 b.record(stream)
                 lat.append((a, b))
             torch.cuda.synchronize()
             lat = [a.elapsed_time(b) for a, b in lat]
             med = float(np.median(lat))
-            rec.update({"order": "apply_then_update", "ms_per_step": round(ms, 4),
+            rec.update({"order": "apply_then_update",
+                        "bf16_copies": "kept in the workspace from frame to frame (the "
+                                       "stream-step EMIT/REUSE flags)",
+                        "ms_per_step": round(ms, 4),
                         "per_frame_ms": round(ms / wl.frames, 5),
                         "tokens_per_s": round(wl.n_kv / (ms / 1e3)),
                         "per_frame_latency_ms": {
@@ -352,10 +355,10 @@ def main():
             return
         if wl.streaming:
             w = [t.clone() for t in ws_layers[0]]
-            for (s, e) in WL.frame_slices(wl):
+            for i, (s, e) in enumerate(WL.frame_slices(wl)):
                 zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
                                renorm=renorm, order=order, out=o[s:e], workspace=ws,
-                               step_rule=rule)
+                               step_rule=rule, emit_bf16=True, reuse_bf16=i > 0)
             return
         for li, wl_w in enumerate(ws_layers):
             if prof is not None:
@@ -433,11 +436,12 @@ def main():
         # per-frame latency: events around every frame's call, in a pass after the timed region
         w = [t.clone() for t in ws_layers[0]]
         evs = []
-        for (s, e) in WL.frame_slices(wl):
+        for i, (s, e) in enumerate(WL.frame_slices(wl)):
             a, b = make_events(torch, 2)
             a.record(stream)
             zm.stream_step(x["q"][s:e], x["k"][s:e], x["v"][s:e], x["eta"][s:e], *w,
-                           renorm=renorm, order=order, out=o[s:e], workspace=ws, step_rule=rule)
+                           renorm=renorm, order=order, out=o[s:e], workspace=ws, step_rule=rule,
+                           emit_bf16=True, reuse_bf16=i > 0)
             b.record(stream)
             evs.append((a, b))
         torch.cuda.synchronize()

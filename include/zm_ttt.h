@@ -90,6 +90,25 @@ typedef enum zm_renorm { ZM_RENORM_NONE = 0, ZM_RENORM_ROW = 1 } zm_renorm;
  * UPDATE_THEN_APPLY writes frame t first and reads it with W(t). */
 typedef enum zm_order { ZM_APPLY_THEN_UPDATE = 0, ZM_UPDATE_THEN_APPLY = 1 } zm_order;
 
+/* Flags OR-ed into the order argument of zm_ttt_stream_step, for a caller that
+ * streams frames through one workspace: the bf16 operand copies of W that a
+ * frame's reduce writes serve the next frame, which then skips its separate
+ * rounding launch (bf16 io; with fp32 io the flags have no effect):
+ *   ZM_STREAM_EMIT_BF16:  on return the workspace holds the bf16 operand
+ *     copies of the state the call leaves in w1, w2, w3;
+ *   ZM_STREAM_REUSE_BF16: the workspace already holds the bf16 operand copies
+ *     of the incoming state, left by the previous call on this workspace with
+ *     ZM_STREAM_EMIT_BF16; the call does not round w1, w2, w3 again.
+ * A stream passes EMIT on its first frame and EMIT | REUSE on the others.
+ * With REUSE the caller guarantees that since that previous call neither the
+ * workspace nor w1, w2, w3 changed and the descriptor is the same; otherwise
+ * the results are undefined (the library keeps no state to check it).  The
+ * results are bitwise those of calls without the flags. */
+typedef enum zm_stream_flags {
+  ZM_STREAM_EMIT_BF16 = 0x100,
+  ZM_STREAM_REUSE_BF16 = 0x200
+} zm_stream_flags;
+
 /* The step taken with the chunk gradient g of one weight matrix (review, the
  * update display after Eq. (3)):
  *   ZM_STEP_GRADIENT:      W' = W - g;
@@ -156,7 +175,8 @@ ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* One streaming step on one frame of n_frame tokens (review 3. Streaming
- * Reconstruction, Eq. (6)).  w1, w2, w3 hold the state W(t-1) on entry and
+ * Reconstruction, Eq. (6)).  order: a zm_order, optionally OR-ed with
+ * zm_stream_flags.  w1, w2, w3 hold the state W(t-1) on entry and
  * W(t) on return (updated in place).  q, k, v: [n_frame, heads, d_head];
  * eta: [n_frame, heads]; o receives f_{W(t-1)}(q) (APPLY_THEN_UPDATE) or
  * f_{W(t)}(q) (UPDATE_THEN_APPLY).  o must not overlap q, k, v or eta: with

@@ -18,6 +18,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
 BF16, F32 = 0, 1
 RENORM_NONE, RENORM_ROW = 0, 1
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
+STREAM_EMIT_BF16, STREAM_REUSE_BF16 = 0x100, 0x200
 STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
@@ -306,9 +307,14 @@ def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, w
 
 
 def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE, out=None,
-                workspace=None, step_rule=STEP_GRADIENT):
+                workspace=None, step_rule=STEP_GRADIENT, emit_bf16=False, reuse_bf16=False):
     """One frame of the streaming recursion; w1, w2, w3 are updated in place.
-    Returns o (read with W(t-1) for APPLY_THEN_UPDATE, W(t) otherwise)."""
+    Returns o (read with W(t-1) for APPLY_THEN_UPDATE, W(t) otherwise).
+    emit_bf16 / reuse_bf16: the STREAM_EMIT_BF16 / STREAM_REUSE_BF16 flags
+    (keep W's bf16 operand copies in `workspace` from one frame to the next;
+    reuse needs the same workspace as the previous emitting call)."""
+    if reuse_bf16 and workspace is None:
+        raise ZmError("reuse_bf16 needs the workspace of the previous call")
     io = _io_of(q, k, v)
     o = out if out is not None else _like_tokens(q)
     n = q.shape[0]
@@ -317,7 +323,9 @@ def stream_step(q, k, v, eta, w1, w2, w3, renorm=False, order=APPLY_THEN_UPDATE,
     _eta(eta, n, desc.heads)
     _on_gpu(q, k, v, o, eta, w1, w2, w3)
     ws, _ = _workspace(desc, n, n, w1.device, workspace)
-    st = load_library().zm_ttt_stream_step(ctypes.byref(desc), int(order), n, _ptr(q), _ptr(k),
+    flags = (STREAM_EMIT_BF16 if emit_bf16 else 0) | (STREAM_REUSE_BF16 if reuse_bf16 else 0)
+    st = load_library().zm_ttt_stream_step(ctypes.byref(desc), int(order) | flags, n, _ptr(q),
+                                           _ptr(k),
                                            _ptr(v), _ptr(eta), _ptr(w1), _ptr(w2), _ptr(w3),
                                            _ptr(o), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
     _check(st, "zm_ttt_stream_step")

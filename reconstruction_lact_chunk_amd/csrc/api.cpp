@@ -31,7 +31,7 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10102;  // 1.1.2
+constexpr int kVersion = 10200;  // 1.2.0
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
@@ -307,19 +307,24 @@ int run_apply(const zm_ttt_desc* d, int64_t n, const void* q, void* o, const flo
 // One chunk of a sequence read and written in the given order (streaming
 // frame or chunk of zm_ttt_chunked): with APPLY_THEN_UPDATE o = f_W(q), then
 // W <- Update(W; chunk) `inner` times; with UPDATE_THEN_APPLY the updates come
-// first.  do_update = false only reads.  W is updated in place.
+// first.  do_update = false only reads.  W is updated in place.  With bf16 io,
+// reuse says that set a of the workspace already holds the bf16 copies of the
+// incoming W (no cast), and emit that set a must hold those of the outgoing W
+// on return (the last reduce writes them).
 int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_t n,
               const void* q, const void* k, const void* v, const float* eta, float* w1, float* w2,
-              float* w3, void* o, Ws ws, hipStream_t st) {
+              float* w3, void* o, Ws ws, hipStream_t st, bool reuse = false, bool emit = false) {
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const Layout L = layout(d, n, n);
   const WSet a = carve_set(ws.p, L.set_a, welems);
   const WSet b = carve_set(ws.p, L.set_b, welems);
   const bool bf16 = d->io_dtype == ZM_BF16;
+  reuse = reuse && bf16;
+  emit = emit && bf16;
   const int updates = do_update ? inner : 0;
   if (order == ZM_APPLY_THEN_UPDATE || updates == 0) {
     // Read the chunk with the incoming W; the first update shares that cast.
-    if (bf16) {
+    if (bf16 && !reuse) {
       Scoped s(kStageCast, st);
       ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
     }
@@ -336,20 +341,26 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
                                  (const uint16_t*)v, eta, n, d->ld_tok, d->heads, d->d_head,
                                  d->d_hidden, a, part, L.plan, st));
       }
-      ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits, nullptr, st));
+      // the frame kernel has read set a before the reduce rewrites it
+      ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits,
+                           (emit && updates == 1) ? &a : nullptr, st));
       first = 1;
     } else {
       ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, ws, st));
     }
     for (int i = first; i < updates; ++i)
-      ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws, nullptr, bf16 && i == 0, st));
+      ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws,
+                        (emit && i == updates - 1) ? &a : nullptr, bf16 && i == 0, st));
     return ZM_OK;
   }
-  // The last update also writes the bf16 copies the read uses.
-  for (int i = 0; i < updates; ++i)
-    ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws,
-                      (bf16 && n > 0 && i == updates - 1) ? &b : nullptr, false, st));
-  return run_apply(d, n, q, o, w1, w2, w3, b, ws, st);
+  // The last update also writes the bf16 copies the read uses (into set a
+  // when they must outlive the call).
+  for (int i = 0; i < updates; ++i) {
+    const WSet* out = nullptr;
+    if (bf16 && i == updates - 1) out = emit ? &a : (n > 0 ? &b : nullptr);
+    ZM_TRY(run_update(d, n, k, v, eta, w1, w2, w3, w1, w2, w3, ws, out, reuse && i == 0, st));
+  }
+  return run_apply(d, n, q, o, w1, w2, w3, emit ? a : b, ws, st);
 }
 
 inline size_t io_bytes(const zm_ttt_desc* d) { return d->io_dtype == ZM_BF16 ? 2 : 4; }
@@ -578,6 +589,8 @@ int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, cons
                        float* w3, void* o, void* workspace, size_t workspace_bytes,
                        void* stream) {
   ZM_TRY(check_desc(desc));
+  const int flags = order & (ZM_STREAM_EMIT_BF16 | ZM_STREAM_REUSE_BF16);
+  order &= ~(ZM_STREAM_EMIT_BF16 | ZM_STREAM_REUSE_BF16);
   if (order != ZM_APPLY_THEN_UPDATE && order != ZM_UPDATE_THEN_APPLY) return ZM_ERR_INVALID_ARG;
   ZM_TRY(check_counts(n_frame, n_frame));
   ZM_TRY(check_tokens(q, n_frame));
@@ -588,7 +601,8 @@ int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, cons
   ZM_TRY(check_weights(w1, w2, w3));
   ZM_TRY(check_ws(desc, n_frame, n_frame, workspace, workspace_bytes));
   return run_chunk(desc, order, true, 1, n_frame, q, k, v, eta, w1, w2, w3, o,
-                   Ws{workspace, workspace_bytes}, (hipStream_t)stream);
+                   Ws{workspace, workspace_bytes}, (hipStream_t)stream,
+                   (flags & ZM_STREAM_REUSE_BF16) != 0, (flags & ZM_STREAM_EMIT_BF16) != 0);
 }
 
 int zm_ttt_layer_workspace_size(const zm_ttt_desc* desc, const zm_layer_weights* lw, int64_t n,

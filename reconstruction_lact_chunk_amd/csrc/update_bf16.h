@@ -83,17 +83,19 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
 
 // SiLU / gate backward for one (token, hidden) element.  x = -log2(e) W1 k
 // (the bf16 W1 copy carries the factor), b = W3 k, e = W2^T (eta v).
-// Returns ga and, scaled by -log2(e), gb and u = SiLU(a) b; the kernel undoes
-// that scale on the dW3 and dW2 partial sums.  With s' = x sig:
-//   sig = 1 / (1 + 2^x),  s = SiLU(a) = -s' / log2(e),
-//   ga = e b (sig + s (1 - sig)),  gb' = e s',  u' = s' b.
+// Returns ga, gb and u = SiLU(a) b, each scaled by -log2(e); the kernel undoes
+// that scale on the partial sums.  With s' = x sig = -log2(e) SiLU(a):
+//   sig = 1 / (1 + 2^x),  u' = s' b,  gb' = e s',
+//   ga' = e (u' + sig (-log2(e) b - u')),
+// the last from ga = e b (sig + s (1 - sig)) = e (u + sig (b - u)), which
+// takes one operation fewer per element than the product form.
 __device__ __forceinline__ void gate_backward(float x, float b, float e, float& ga, float& gb,
                                               float& u) {
   const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
   const float sp = x * sg;
   u = sp * b;
   gb = e * sp;
-  ga = (e * b) * fmaf(fmaf(-sp, sg, sp), kNegInvLog2e, sg);
+  ga = e * fmaf(sg, fmaf(kNegLog2e, b, -u), u);
 }
 
 // The work of update block `blk` (one workgroup of 512 threads): the kernels
@@ -297,23 +299,23 @@ __device__ __forceinline__ void update_tiles(
   // and one micro-step follows each MFMA: on gfx950 about that much VALU work
   // issues in the shadow of a 16x16x32 MFMA, while longer VALU runs stall
   // the matrix core.  Element rows are processed in pairs (two independent
-  // chains), 14 micro-steps per pair; the steps left over after the last
+  // chains), 13 micro-steps per pair; the steps left over after the last
   // MFMA, then staging of tile t + 2 and one barrier close the iteration.
   // Every gate value is pinned where it is computed so that the compiler
   // keeps this placement.  The loop is unrolled by two so the carried state
   // alternates between two register sets instead of being copied.
-  constexpr int NMICRO = 4 * 14;
+  constexpr int NMICRO = 4 * 13;
   auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur, bool barrier)
       __attribute__((always_inline)) {
     fetch(t + 3);
     Frag2 fr[NSLOT];
 #pragma unroll
     for (int j = 0; j < LA; ++j) fr[j] = load_slot(t, j);
-    float g_t[2], g_sg[2], g_sp[2], g_u[2], g_gb[2], g_w[2], g_eb[2], g_ga[2];
+    float g_t[2], g_sg[2], g_sp[2], g_u[2], g_gb[2], g_w[2], g_ga[2];
     u32x4 gap, gbp, up;
     auto micro = [&](int i) __attribute__((always_inline)) {
       if (i >= NMICRO) return;
-      const int pr = i / 14, k = i % 14;
+      const int pr = i / 13, k = i % 13;
       auto el = [&](int h, auto&& fn2) __attribute__((always_inline)) {
         const int r = 2 * pr + h, mb = r >> 2, q = r & 3;
         fn2(h, f.a[mb][q], f.b[mb][q], f.e[mb][q]);
@@ -345,27 +347,23 @@ __device__ __forceinline__ void update_tiles(
           break;
         case 8:
           for (int h = 0; h < 2; ++h)
-            el(h, [&](int hh, float, float, float) {
-              g_w[hh] = fmaf(-g_sp[hh], g_sg[hh], g_sp[hh]);
+            el(h, [&](int hh, float, float b, float) {
+              g_w[hh] = fmaf(kNegLog2e, b, -g_u[hh]);
               pin(g_w[hh]);
             });
           break;
         case 9:
           for (int h = 0; h < 2; ++h)
             el(h, [&](int hh, float, float, float) {
-              g_w[hh] = fmaf(g_w[hh], kNegInvLog2e, g_sg[hh]);
+              g_w[hh] = fmaf(g_sg[hh], g_w[hh], g_u[hh]);
               pin(g_w[hh]);
             });
           break;
         case 10:
           for (int h = 0; h < 2; ++h)
-            el(h, [&](int hh, float, float b, float e) { g_eb[hh] = e * b; pin(g_eb[hh]); });
+            el(h, [&](int hh, float, float, float e) { g_ga[hh] = e * g_w[hh]; pin(g_ga[hh]); });
           break;
-        case 11:
-          for (int h = 0; h < 2; ++h)
-            el(h, [&](int hh, float, float, float) { g_ga[hh] = g_eb[hh] * g_w[hh]; pin(g_ga[hh]); });
-          break;
-        case 12: {
+        case 11: {
           unsigned pa = pack_bf16x2(g_ga[0], g_ga[1]), pb = pack_bf16x2(g_gb[0], g_gb[1]);
           pin(pa);
           pin(pb);
@@ -449,9 +447,10 @@ __device__ __forceinline__ void update_tiles(
     }
     backward(ntiles - 1, ga_);
   }
-  // dW3 and dW2 were accumulated from gb' and u', which carry -log2(e)
+  // all three partial sums were accumulated from ga', gb', u', which carry -log2(e)
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
+    acc1[m] *= kNegInvLog2e;
     acc3[m] *= kNegInvLog2e;
     acc2[m] *= kNegInvLog2e;
   }

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10102
+    assert zm.version() == 10200
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -419,3 +419,20 @@ def test_undersized_workspaces_are_rejected_before_any_launch():
         assert st == zm.ERR_WORKSPACE, (n_kv, n_q)
     assert L.zm_ttt_apply(ctypes.byref(wd), 131_073, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD,
                           ws_size(wd, 0, 100_000)[1], None) == zm.ERR_WORKSPACE
+
+
+def test_stream_flags_are_validated_with_the_order():
+    L = lib()
+    de = desc()
+    need = ws_size(de, 100, 100)[1]
+    args = (GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, GOOD)
+    # unknown bits around the two flags are rejected before any HIP call
+    for order in (0x400, 0x101 | 0x800, 0x1000, 2 | zm.STREAM_EMIT_BF16):
+        assert L.zm_ttt_stream_step(ctypes.byref(de), order, 100, *args, need, None) == \
+            zm.ERR_INVALID_ARG, hex(order)
+    # a valid order with flags still runs the other checks (bad eta pointer here)
+    assert L.zm_ttt_stream_step(ctypes.byref(de), 1 | zm.STREAM_EMIT_BF16 | zm.STREAM_REUSE_BF16,
+                                100, GOOD, GOOD, GOOD, None, GOOD, GOOD, GOOD, GOOD, GOOD, need,
+                                None) == zm.ERR_INVALID_ARG
+    with pytest.raises(zm.ZmError, match="reuse_bf16"):
+        zm.stream_step(*[torch.zeros(1)] * 7, reuse_bf16=True)

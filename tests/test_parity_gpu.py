@@ -69,6 +69,16 @@ class Inputs:
         return host(self.t[k])
 
 
+def sampled_units(d_hidden, rng, block=16, blocks=None):
+    """Hidden units for a sampled check: one drawn from each run of `block`
+    consecutive units (every wave's 16-unit block of both 128-unit workgroup
+    slices at hidden 256), or from `blocks` equal runs when given."""
+    if blocks is not None:
+        block = d_hidden // blocks
+    starts = np.arange(0, d_hidden, block)
+    return np.sort(starts + rng.integers(0, block, len(starts)))
+
+
 def check(name, x, ref, tol):
     r = rel(x, ref)
     say(f"    {name}: rel {r:.3e} (tol {tol:.0e})")
@@ -275,7 +285,9 @@ def test_bitwise_determinism(io):
 def test_f700_full_size_sampled(layer):
     """The 700-frame workload in the launch configuration the benchmark
     times (layer 23: the last layer of the 24-layer stack, fresh weights),
-    checked on sampled rows of W_hat and sampled query outputs."""
+    checked on every head: 16 sampled hidden units per head (one in each wave's
+    16-unit block of both 128-unit workgroup slices) of W_hat, and sampled
+    query outputs."""
     wl = WL.WORKLOADS["f700"]
     say(f"case f700 full size seed=4 layer={layer} (sampled checks)")
     inp = Inputs(wl, 4)
@@ -289,9 +301,9 @@ def test_f700_full_size_sampled(layer):
                                       t["w3"], renorm=False)
     torch.cuda.synchronize()
     rng = np.random.default_rng(0)
-    heads = [0, 5]
+    heads = list(range(wl.heads))
     for hd in heads:
-        J = np.sort(rng.choice(wl.d_hidden, 3, replace=False))
+        J = sampled_units(wl.d_hidden, rng)   # 16 units: one per wave block, both slices
         k = host(t["k"][:, hd])
         v = host(t["v"][:, hd])
         eta = host(t["eta"][:, hd])

@@ -13,7 +13,7 @@ import torch
 import oracle
 import reconstruction_lact_chunk_amd as zm
 import workloads as WL
-from test_parity_gpu import TOL, Inputs, check, host, say
+from test_parity_gpu import TOL, Inputs, check, host, sampled_units, say
 
 pytestmark = pytest.mark.gpu
 D, H_ = 1024, 2048
@@ -137,7 +137,7 @@ def test_wide_fw100_full_size_sampled():
     (f1, f2, f3) = zm.update(t["k"], t["v"], t["eta"], t["w1"], t["w2"], t["w3"], renorm=False)
     torch.cuda.synchronize()
     rng = np.random.default_rng(1)
-    J = np.sort(rng.choice(H_, 4, replace=False))
+    J = sampled_units(H_, rng, blocks=32)   # 32 units, one in each run of 64
     k, v, eta = host(t["k"][:, 0]), host(t["v"][:, 0]), host(t["eta"][:, 0])
     w1, w2, w3 = host(t["w1"][0]), host(t["w2"][0]), host(t["w3"][0])
     s1, s2, s3 = oracle.update_rows_sampled(k, v, eta, w1, w2, w3, J)
