@@ -69,6 +69,9 @@
 extern "C" {
 #endif
 
+/* Size of the device scratch array behind zm_ttt_update_apply_scratch. */
+#define ZM_TTT_SCRATCH_BYTES ((size_t)64 << 20)
+
 typedef enum zm_status {
   ZM_OK = 0,
   ZM_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, bad size or enum */
@@ -173,6 +176,27 @@ ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
                         const float* w1, const float* w2, const float* w3,
                         float* w1_out, float* w2_out, float* w3_out, void* o,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * update and apply as zm_ttt_update_apply, run in a scratch array the library
+ * holds in device memory (ZM_TTT_SCRATCH_BYTES = 64 MiB, one copy per GPU
+ * from module load to process end) instead of a caller workspace.  The
+ * call allocates nothing; on its first use on a device it looks up that
+ * device's scratch address.  Results are bitwise those of
+ * zm_ttt_update_apply.  Narrow heads only: a call whose workspace need
+ * (zm_ttt_workspace_size(desc, n_kv, n_q)) exceeds the scratch returns
+ * ZM_ERR_WORKSPACE, and the full-width shape ZM_ERR_UNSUPPORTED.  Nothing in
+ * the scratch needs clearing (every kernel writes what the next one reads),
+ * and a call leaves its last contents there.  All calls on one GPU share its
+ * scratch: calls that overlap in time on one GPU (two streams, two threads)
+ * race and give undefined results; order them on one stream. */
+ZM_API int zm_ttt_update_apply_scratch(const zm_ttt_desc* desc, int64_t n_kv,
+                                const void* k, const void* v, const float* eta,
+                                int64_t n_q, const void* q,
+                                const float* w1, const float* w2, const float* w3,
+                                float* w1_out, float* w2_out, float* w3_out, void* o,
+                                void* stream);
 
 /* One streaming step on one frame of n_frame tokens (review 3. Streaming
  * Reconstruction, Eq. (6)).  order: a zm_order, optionally OR-ed with

@@ -19,10 +19,12 @@ BF16, F32 = 0, 1
 RENORM_NONE, RENORM_ROW = 0, 1
 APPLY_THEN_UPDATE, UPDATE_THEN_APPLY = 0, 1
 STREAM_EMIT_BF16, STREAM_REUSE_BF16 = 0x100, 0x200
+SCRATCH_BYTES = 64 << 20  # ZM_TTT_SCRATCH_BYTES
 STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
     "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
+    "zm_ttt_update_apply_scratch",
     "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size", "zm_ttt_layer",
     "zm_status_string", "zm_ttt_last_error", "zm_ttt_version", "zm_ttt_set_profile_events",
 )
@@ -80,6 +82,8 @@ def load_library(path: str | None = None):
     lib.zm_ttt_apply.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.zm_ttt_update_apply.argtypes = [_DESC, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _SZ, _P]
+    lib.zm_ttt_update_apply_scratch.argtypes = [_DESC, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P,
+                                                _P, _P, _P, _P]
     lib.zm_ttt_stream_step.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _P, _P,
                                        _P, _SZ, _P]
     lib.zm_ttt_chunked.argtypes = [_DESC, ctypes.c_int, _I64, _P, _P, ctypes.c_int, _P, _P, _P,
@@ -95,6 +99,7 @@ def load_library(path: str | None = None):
     lib.zm_ttt_version.argtypes = []
     lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
     for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
+                 "zm_ttt_update_apply_scratch",
                  "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size",
                  "zm_ttt_layer", "zm_ttt_version", "zm_ttt_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
@@ -303,6 +308,28 @@ def update_apply(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None, w
         ctypes.byref(desc), n_kv, _ptr(k), _ptr(v), _ptr(eta), n_q, _ptr(q), _ptr(w1), _ptr(w2),
         _ptr(w3), *map(_ptr, outs), _ptr(o), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
     _check(st, "zm_ttt_update_apply")
+    return outs, o
+
+
+def update_apply_scratch(k, v, eta, q, w1, w2, w3, renorm=False, w_out=None, out=None,
+                         step_rule=STEP_GRADIENT):
+    """update_apply run in the library's own device scratch instead of a
+    workspace (zm_ttt_update_apply_scratch: for callers that cannot allocate;
+    narrow heads, at most SCRATCH_BYTES of workspace need).  The outputs are
+    allocated here unless w_out / out are given; pass them to allocate nothing."""
+    io = _io_of(k, v, q)
+    o = out if out is not None else _like_tokens(q)
+    n_kv, n_q = k.shape[0], q.shape[0]
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, q, o, step_rule=step_rule,
+                     rows=[n_kv, n_kv, n_q, n_q], check_device=False)
+    _eta(eta, n_kv, desc.heads)
+    outs = w_out if w_out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_out_weights(outs, w1, w2, w3)
+    _on_gpu(k, v, eta, q, o, w1, w2, w3, *outs)
+    st = load_library().zm_ttt_update_apply_scratch(
+        ctypes.byref(desc), n_kv, _ptr(k), _ptr(v), _ptr(eta), n_q, _ptr(q), _ptr(w1), _ptr(w2),
+        _ptr(w3), *map(_ptr, outs), _ptr(o), _stream(w1.device))
+    _check(st, "zm_ttt_update_apply_scratch")
     return outs, o
 
 

@@ -9,6 +9,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "gemm_lt.h"
 #include "layer_kernels.h"
 #include "wide_path.h"
@@ -480,6 +483,56 @@ int check_layer_args(const zm_ttt_desc* d, const zm_layer_weights* lw, int64_t n
   return check_counts(n, n);
 }
 
+// ---- library-owned scratch for zm_ttt_update_apply_scratch -----------------
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops) run update + apply in this fixed device array instead
+// of a workspace they pass in.  Every GPU the library runs on holds one copy
+// of it, at its own address, from module load until the process ends.  In
+// host code the array's name is not a device address: kernels get the
+// address hipGetSymbolAddress returns for the current device, taken once per
+// device and kept below.
+constexpr size_t kScratchBytes = ZM_TTT_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+// Device address of the current device's copy of `scratch` (looked up on the
+// first call for each device, with that device current).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_last_error("hipGetDevice: %s (%d)", hipGetErrorString(e), (int)e);
+    return ZM_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    set_last_error("device %d beyond the %d devices the scratch table covers", dev,
+                   kMaxScratchDevices);
+    return ZM_ERR_UNSUPPORTED;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (es != hipSuccess || p == nullptr) {
+        set_last_error("hipGetSymbolAddress(scratch): %s (%d)", hipGetErrorString(es), (int)es);
+        return ZM_ERR_HIP;
+      }
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ZM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -582,6 +635,38 @@ int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv, const void* k, co
   ZM_TRY(run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out, ws,
                     (bf16 && n_q > 0) ? &b : nullptr, false, st));
   return run_apply(desc, n_q, q, o, w1_out, w2_out, w3_out, b, ws, st);
+}
+
+int zm_ttt_update_apply_scratch(const zm_ttt_desc* desc, int64_t n_kv, const void* k,
+                                const void* v, const float* eta, int64_t n_q, const void* q,
+                                const float* w1, const float* w2, const float* w3,
+                                float* w1_out, float* w2_out, float* w3_out, void* o,
+                                void* stream) {
+  ZM_TRY(check_desc(desc));
+  ZM_TRY(check_counts(n_kv, n_q));
+  // the full-width shape needs GEMM-library handles and token-block buffers
+  // far beyond the scratch
+  if (is_wide(desc)) {
+    set_last_error("the full-width head has no scratch variant");
+    return ZM_ERR_UNSUPPORTED;
+  }
+  const size_t need = layout(desc, n_kv, n_q).total;
+  if (need > kScratchBytes) {
+    set_last_error("update over %lld tokens needs %zu bytes of scratch, the library holds %zu",
+                   (long long)n_kv, need, kScratchBytes);
+    return ZM_ERR_WORKSPACE;
+  }
+  ZM_TRY(check_tokens(k, n_kv));
+  ZM_TRY(check_tokens(v, n_kv));
+  ZM_TRY(check_eta(eta, n_kv));
+  ZM_TRY(check_tokens(q, n_q));
+  ZM_TRY(check_tokens(o, n_q));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_weights(w1_out, w2_out, w3_out));
+  void* ws = nullptr;
+  ZM_TRY(scratch_for_current_device(&ws));
+  return zm_ttt_update_apply(desc, n_kv, k, v, eta, n_q, q, w1, w2, w3, w1_out, w2_out, w3_out,
+                             o, ws, kScratchBytes, stream);
 }
 
 int zm_ttt_stream_step(const zm_ttt_desc* desc, int order, int64_t n_frame, const void* q,

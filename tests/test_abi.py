@@ -436,3 +436,37 @@ def test_stream_flags_are_validated_with_the_order():
                                 None) == zm.ERR_INVALID_ARG
     with pytest.raises(zm.ZmError, match="reuse_bf16"):
         zm.stream_step(*[torch.zeros(1)] * 7, reuse_bf16=True)
+
+
+def test_scratch_entry_point_limits_before_any_hip_call():
+    L = lib()
+    args = (GOOD, GOOD, GOOD)
+    # a call needing more workspace than the library's scratch: refused on the
+    # host.  The split count is capped by the compute units, so the need stops
+    # growing with n (8 heads of 128 / 256: 54.5 MB at any length); 64 heads
+    # need 84 MB.
+    de = desc()
+    many_heads = desc(heads=64)
+    assert ws_size(many_heads, 100_000, 0)[1] > zm.SCRATCH_BYTES
+    assert L.zm_ttt_update_apply_scratch(ctypes.byref(many_heads), 100_000, *args, 0, GOOD, GOOD,
+                                         GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, None) == \
+        zm.ERR_WORKSPACE
+    assert "scratch" in zm.last_error()
+    # the full-width head has no scratch variant
+    wd = desc(heads=1, d=1024, h=2048)
+    assert L.zm_ttt_update_apply_scratch(ctypes.byref(wd), 10, *args, 10, GOOD, GOOD, GOOD, GOOD,
+                                         GOOD, GOOD, GOOD, GOOD, None) == zm.ERR_UNSUPPORTED
+    # the usual argument checks (null q with queries)
+    assert L.zm_ttt_update_apply_scratch(ctypes.byref(de), 100, *args, 100, None, GOOD, GOOD,
+                                         GOOD, GOOD, GOOD, GOOD, GOOD, None) == zm.ERR_INVALID_ARG
+    assert L.zm_ttt_update_apply_scratch(None, 100, *args, 100, GOOD, GOOD, GOOD, GOOD, GOOD,
+                                         GOOD, GOOD, GOOD, None) == zm.ERR_INVALID_ARG
+    # the largest 700-frame layer fits
+    f700 = ws_size(de, 961_800, 961_800)[1]
+    assert f700 <= zm.SCRATCH_BYTES
+
+
+def test_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ZM_TTT_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == zm.SCRATCH_BYTES
