@@ -419,6 +419,13 @@ def test_apply_tiles_conflict_free(D, H):
             # head width 64: 136-byte rows put two rows' pieces of one half-wave
             # on 34 slots of 32, so one pair collides (2-way); 128: conflict-free
             assert read_b64_degree(addrs) == (1 if D == 128 else 2)
+        # the two halves merged into one 16-byte access per lane (ds_read2_b64)
+        # would be 2-way conflicted at the 128 shape: two rows share each bank
+        # group of a 16-byte read.  Measured: 1.54e7 conflict cycles per f700
+        # launch merged, 0 with the halves as separate reads.
+        merged = [2 * (((64 * w + l) // cpt) * OP + 8 * ((64 * w + l) % cpt)) for l in range(64)]
+        if D == 128:
+            assert read_b128_degree(merged) == 2
 
 
 # ---------------------------------------------------------------------------
