@@ -165,11 +165,14 @@ ZM_API int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q,
                  const float* w1, const float* w2, const float* w3,
                  void* o, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bidirectional single chunk: the update over all n_kv tokens, then the
- * apply of all n_q queries through W_hat (the queries may include extra
- * target-view rows beyond the image tokens).  Outputs W_hat to w*_out (may
- * alias w*) and o.  Equivalent to zm_ttt_update followed by zm_ttt_apply on
- * W_hat, without re-reading W_hat from fp32. */
+/* Bidirectional single chunk (review of ZipMap, Method 2: the chunk update of
+ * Eq. (3) over all image tokens, then the read of Eq. (4) with the updated
+ * weights; the ZipMap notes' TTT-module section describes the same write-then-
+ * read of one chunk; a ray-map target view only reads): the update over all
+ * n_kv tokens, then the apply of all n_q queries through W_hat (the queries
+ * may include extra target-view rows beyond the image tokens).  Outputs W_hat
+ * to w*_out (may alias w*) and o.  Equivalent to zm_ttt_update followed by
+ * zm_ttt_apply on W_hat, without re-reading W_hat from fp32. */
 ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
                         const void* k, const void* v, const float* eta,
                         int64_t n_q, const void* q,
