@@ -543,8 +543,9 @@ def main():
         fl_dom = units[dom][0]
         ach = fl_dom / (avg[dom] / 1e3) / 1e12
         if wide:
-            kname = ("update stage (hipBLASLt GEMMs + k_wide_gate_update)" if dom == "update"
-                     else "apply stage (hipBLASLt GEMMs + k_wide_gate_apply)")
+            kname = ("update stage (hipBLASLt E and reduction GEMMs + k_wide_rows update)"
+                     if dom == "update" else
+                     "apply stage (k_wide_rows read + hipBLASLt output GEMM)")
         else:
             kname = "k_update_bf16<128,256>" if dom == "update" else "k_apply_bf16<128,256>"
         result["roofline"] = {

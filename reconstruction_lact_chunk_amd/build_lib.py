@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libzmttt.so")
 ARCH = "gfx950"
 
 SOURCES = ["weights.hip", "update_bf16.hip", "apply_bf16.hip", "frame_bf16.hip", "fp32_path.hip",
-           "newton_schulz.hip", "wide_kernels.hip", "wide_path.cpp", "gemm_lt.cpp",
+           "newton_schulz.hip", "wide_kernels.hip", "wide_gemm.hip", "wide_path.cpp", "gemm_lt.cpp",
            "layer_kernels.hip", "wide_ns.hip", "api.cpp"]
 
 COMMON = [

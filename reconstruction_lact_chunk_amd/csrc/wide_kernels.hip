@@ -1,85 +1,13 @@
-// Elementwise and reduction kernels of the full-width fast weight (one head
-// of d = 1024, hidden h = 2048: the 6 d^2 state of the ZipMap paper-reading
-// notes' state-size paragraph).  The dense products of that shape run as
-// library GEMMs (wide_path.cpp); these kernels do the rest:
-//   k_wide_gate_update  SiLU / gate backward of the chunk gradient, in place
-//                       on the forward products of a token block;
-//   k_wide_gate_apply   the read's gate u = SiLU(W1 q) (*) W3 q, in place;
-//   k_wide_reduce       fixed-order sum of the block partials, the step, the
-//                       row renorm and the bf16 operand copies, one workgroup
-//                       per weight row (rows of 1024 or 2048 elements).
-// Formulas: review of ZipMap (kimjy99.github.io), Method 2, Eq. (1)-(4) and
-// the renormalised update display after Eq. (3).
+// Reduction kernel of the full-width fast weight (one head of d = 1024, hidden
+// h = 2048: the 6 d^2 state of the ZipMap paper-reading notes' state-size
+// paragraph): k_wide_reduce, the fixed-order sum of the block partials, the
+// step, the row renorm and the bf16 operand copies, one workgroup per weight
+// row (rows of 1024 or 2048 elements).  Formulas: review of ZipMap
+// (kimjy99.github.io), Method 2, Eq. (1)-(4) and the renormalised update
+// display after Eq. (3).
 #include "wide_path.h"
 
 namespace zm {
-
-// Forward products of one token block, bf16, row t:
-//   ab[t][j]     = x_j = -log2(e) (W1 k_t)_j   (the bf16 W1 copy carries the factor)
-//   ab[t][h + j] = (W3 k_t)_j
-//   e[t][j]      = (W2^T v_t)_j
-// Replaced in place by the operands of the chunk-reduction products:
-//   ab[t][j]     = ga = eta e b SiLU'(a)
-//   ab[t][h + j] = gb = eta e SiLU(a)
-//   e[t][j]      = eta u = eta SiLU(a) b
-// with a = W1 k, sig = 1 / (1 + 2^x), SiLU(a) = a sig, SiLU'(a) = sig (1 + a (1 - sig)).
-// One thread per 4 consecutive hidden units of one token.
-__global__ __launch_bounds__(256) void k_wide_gate_update(uint16_t* __restrict__ ab,
-                                                          uint16_t* __restrict__ e,
-                                                          const float* __restrict__ eta,
-                                                          int64_t eta_stride, int64_t tokens,
-                                                          int h) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int q4 = h / 4;
-  if (i >= tokens * q4) return;
-  const int64_t t = i / q4;
-  const int j = 4 * (int)(i - t * q4);
-  uint16_t* pa = ab + t * 2 * h + j;
-  uint16_t* pb = pa + h;
-  uint16_t* pe = e + t * h + j;
-  const u32x2 xa = *(const u32x2*)pa, xb = *(const u32x2*)pb, xe = *(const u32x2*)pe;
-  const float et = eta[t * eta_stride];
-  float ga[4], gb[4], ue[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const unsigned wa = xa[q >> 1], wb = xb[q >> 1], we = xe[q >> 1];
-    const float x = (q & 1) ? bf16hi(wa) : bf16lo(wa);
-    const float b = (q & 1) ? bf16hi(wb) : bf16lo(wb);
-    const float ee = et * ((q & 1) ? bf16hi(we) : bf16lo(we));
-    const float a = x * kNegInvLog2e;
-    const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x));
-    const float s = a * sg;
-    ga[q] = ee * b * (sg + s * (1.f - sg));
-    gb[q] = ee * s;
-    ue[q] = et * s * b;
-  }
-  *(u32x2*)pa = u32x2{pack_bf16x2(ga[0], ga[1]), pack_bf16x2(ga[2], ga[3])};
-  *(u32x2*)pb = u32x2{pack_bf16x2(gb[0], gb[1]), pack_bf16x2(gb[2], gb[3])};
-  *(u32x2*)pe = u32x2{pack_bf16x2(ue[0], ue[1]), pack_bf16x2(ue[2], ue[3])};
-}
-
-// Read gate: ab[t][j] = x = -log2(e) W1 q, ab[t][h + j] = W3 q  ->
-// ab[t][j] = x sig(a) b = -log2(e) u (the bf16 W2 copy used next carries
-// -1 / log2(e)).  One thread per 4 hidden units.
-__global__ __launch_bounds__(256) void k_wide_gate_apply(uint16_t* __restrict__ ab,
-                                                         int64_t tokens, int h) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int q4 = h / 4;
-  if (i >= tokens * q4) return;
-  const int64_t t = i / q4;
-  const int j = 4 * (int)(i - t * q4);
-  uint16_t* pa = ab + t * 2 * h + j;
-  const u32x2 xa = *(const u32x2*)pa, xb = *(const u32x2*)(pa + h);
-  float u[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const unsigned wa = xa[q >> 1], wb = xb[q >> 1];
-    const float x = (q & 1) ? bf16hi(wa) : bf16lo(wa);
-    const float b = (q & 1) ? bf16hi(wb) : bf16lo(wb);
-    u[q] = x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(x)) * b;
-  }
-  *(u32x2*)pa = u32x2{pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3])};
-}
 
 // Sum over the 256 threads of a workgroup, the same bits on every thread:
 // butterflies within each wave, then the four wave sums in a fixed order.
@@ -182,23 +110,6 @@ __global__ __launch_bounds__(256) void k_wide_reduce(const float* __restrict__ p
       }
     }
   }
-}
-
-hipError_t launch_wide_gate_update(uint16_t* ab, uint16_t* e, const float* eta,
-                                   int64_t eta_stride, int64_t tokens, int h, hipStream_t st) {
-  const int64_t items = tokens * (h / 4);
-  if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_wide_gate_update, dim3((unsigned)ceil_div(items, 256)), dim3(256), 0, st,
-                     ab, e, eta, eta_stride, tokens, h);
-  return hipGetLastError();
-}
-
-hipError_t launch_wide_gate_apply(uint16_t* ab, int64_t tokens, int h, hipStream_t st) {
-  const int64_t items = tokens * (h / 4);
-  if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_wide_gate_apply, dim3((unsigned)ceil_div(items, 256)), dim3(256), 0, st,
-                     ab, tokens, h);
-  return hipGetLastError();
 }
 
 hipError_t launch_wide_reduce(const float* part, int splits, int heads, int d, int h,

@@ -4,14 +4,18 @@
 // not fit a compute unit, so the fused register-resident kernels of the
 // narrow heads do not apply.  The layer runs per token block of at most
 // kWideBlock tokens as
-//   update: A = K W1^T, B = K W3^T, E = V W2        (library GEMMs, bf16 out)
-//           gate backward in place                   (k_wide_gate_update)
-//           D13 = [Ga Gb]^T K, D2 = V^T (eta U)      (library GEMMs, fp32 partials)
+//   update: E = V W2                                  (library GEMM, bf16 out)
+//           [Ga Gb], eta U from K W1^T, K W3^T, E and eta: the two products
+//           with the gate backward in their epilogue   (k_wide_rows, update)
+//           D13 = [Ga Gb]^T K, D2 = V^T (eta U)        (library GEMMs, fp32 partials)
 //           then the fixed-order reduce / step / renorm over the blocks;
-//   apply:  A = Q W1^T, B = Q W3^T; U = SiLU(A) (*) B; O = U W2^T.
-// The dense products are plain GEMMs and go to hipBLASLt (gemm_lt.cpp: bf16
-// operands, fp32 accumulation); the token sum is combined in a fixed order
-// (bitwise reproducible).
+//   apply:  U' = -log2(e) SiLU(Q W1^T) (*) Q W3^T: the two products with the
+//           gate in their epilogue                     (k_wide_rows, read)
+//           O = U' W2'^T                               (library GEMM).
+// The products that feed a gate are hand-written (wide_gemm.hip: the gate
+// runs on the accumulators, so x and b never reach memory); the plain
+// products go to hipBLASLt (gemm_lt.cpp: bf16 operands, fp32 accumulation).
+// The token sum is combined in a fixed order (bitwise reproducible).
 #include "wide_path.h"
 
 #include "gemm_lt.h"
@@ -31,19 +35,6 @@ bool rm_tn(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const vo
            int count = 1, int64_t sa = 0, int64_t sb = 0, int64_t sc = 0, float beta = 0.f) {
   return lt_rm_tn(M, N, K, A, lda, B, ldb, C, ldc, out_f32, LtWs{w.lt_ws, w.lt_ws_bytes}, st,
                   count, sa, sb, sc, beta);
-}
-
-// [x | b] rows of the token-block buffer: x = tokens (-log2(e) W1)^T and
-// b = tokens W3^T, [len][2 h].  With one head the bf16 W1 and W3 copies are
-// adjacent in the workspace, i.e. [W1; W3] is one [2 h][d] operand and the
-// two products are one GEMM.
-bool forward_w13(int64_t len, int h, int d, const uint16_t* tok, int64_t ld, const WSet& wb,
-                 int hd, int heads, uint16_t* ab, const WideBufs& w, hipStream_t st) {
-  const int64_t hd_elems = (int64_t)h * d;
-  if (heads == 1 && wb.w3b == wb.w1b + hd_elems)
-    return rm_nt(len, 2 * h, d, tok, ld, wb.w1b, d, ab, 2 * h, false, w, st);
-  return rm_nt(len, h, d, tok, ld, wb.w1b + hd * hd_elems, d, ab, 2 * h, false, w, st) &&
-         rm_nt(len, h, d, tok, ld, wb.w3b + hd * hd_elems, d, ab + h, 2 * h, false, w, st);
 }
 
 }  // namespace
@@ -102,13 +93,17 @@ int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* 
       const uint16_t* kb = k + s0 * ld + (int64_t)hd * d;
       const uint16_t* vb = v + s0 * ld + (int64_t)hd * d;
       float* slot = w.part + (int64_t)hd * 3 * hd_elems;
-      // forward on the keys: x = -log2(e) W1 k, b = W3 k, e = W2^T v
-      if (!forward_w13(len, h, d, kb, ld, wb, hd, heads, ab, w, st) ||
-          !rm_nt(len, h, d, vb, ld, wb.w2tb + hd * hd_elems, d, e, h, false, w, st))
+      // forward on the values, e = W2^T v (bf16, a plain library product),
+      // then the W1 / W3 products on the keys with the gate backward in their
+      // epilogue: ga, gb into ab, eta u over e
+      if (!rm_nt(len, h, d, vb, ld, wb.w2tb + hd * hd_elems, d, e, h, false, w, st))
         return ZM_ERR_HIP;
-      const hipError_t ge = launch_wide_gate_update(ab, e, eta + s0 * heads + hd, heads, len, h, st);
+      const hipError_t ge = launch_wide_fwd_gate_update(kb, ld, len, wb.w1b + hd * hd_elems,
+                                                        wb.w3b + hd * hd_elems, d, h,
+                                                        eta + s0 * heads + hd, heads, ab, 2 * h,
+                                                        e, h, st);
       if (ge != hipSuccess) {
-        set_last_error("wide gate (update) launch: %s", hipGetErrorString(ge));
+        set_last_error("wide forward+gate (update) launch: %s", hipGetErrorString(ge));
         return ZM_ERR_HIP;
       }
       // minus the gradient over this block: [D1; D3] = [Ga Gb]^T K, D2 = V^T (eta U).
@@ -147,10 +142,12 @@ int wide_apply(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* q
       const int64_t len = (n - s0) < kWideBlock ? (n - s0) : kWideBlock;
       const uint16_t* qb = q + s0 * ld + (int64_t)hd * d;
       uint16_t* ob = o + s0 * ld + (int64_t)hd * d;
-      if (!forward_w13(len, h, d, qb, ld, wb, hd, heads, w.ab, w, st)) return ZM_ERR_HIP;
-      const hipError_t ge = launch_wide_gate_apply(w.ab, len, h, st);
+      // U' = -log2(e) SiLU(W1 q) (*) W3 q in one kernel, into the block buffer
+      const hipError_t ge = launch_wide_fwd_gate_apply(qb, ld, len, wb.w1b + hd * hd_elems,
+                                                       wb.w3b + hd * hd_elems, d, h, w.ab, 2 * h,
+                                                       st);
       if (ge != hipSuccess) {
-        set_last_error("wide gate (apply) launch: %s", hipGetErrorString(ge));
+        set_last_error("wide forward+gate (apply) launch: %s", hipGetErrorString(ge));
         return ZM_ERR_HIP;
       }
       // O = U' (-W2 / log2(e))^T with U' = -log2(e) U

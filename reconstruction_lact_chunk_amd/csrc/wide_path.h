@@ -1,6 +1,7 @@
 // Full-width fast weight (d = 1024, h = 2048): token-block orchestration of
-// library GEMMs and the wide elementwise / reduce kernels.  Used by the C-ABI
-// layer when the descriptor names that shape.
+// the hand-written forward + gate kernels (wide_gemm.hip), the plain library
+// GEMMs and the reduce kernel (wide_kernels.hip).  Used by the C-ABI layer
+// when the descriptor names that shape.
 #pragma once
 
 #include "zm_ttt.h"
@@ -48,9 +49,21 @@ int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* 
 int wide_apply(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* q, uint16_t* o,
                const WSet& wb, const WideBufs& w, hipStream_t st);
 
-hipError_t launch_wide_gate_update(uint16_t* ab, uint16_t* e, const float* eta,
-                                   int64_t eta_stride, int64_t tokens, int h, hipStream_t st);
-hipError_t launch_wide_gate_apply(uint16_t* ab, int64_t tokens, int h, hipStream_t st);
+// U' = -log2(e) SiLU(W1 q) (*) W3 q for n query rows (stride ldq), W1 copy w1
+// (carrying -log2(e)) and w3 [h][d] bf16, into u (rows of stride ldu), as one
+// hand-written product with the gate in its epilogue (wide_gemm.hip).
+hipError_t launch_wide_fwd_gate_apply(const uint16_t* q, int64_t ldq, int64_t n,
+                                      const uint16_t* w1, const uint16_t* w3, int d, int h,
+                                      uint16_t* u, int64_t ldu, hipStream_t st);
+// The update's W1 / W3 products on key rows k (stride ldk) with the gate
+// backward in their epilogue: from the bf16 W1 (carrying -log2(e)) and W3
+// copies [h][d], e = W2^T v in e[t][j] (stride lde, bf16) and rates eta [n]
+// (stride eta_ld), writes ga to gab[t][j], gb to gab[t][h + j] (rows of stride
+// ldab) and eta u over e (wide_gemm.hip).
+hipError_t launch_wide_fwd_gate_update(const uint16_t* k, int64_t ldk, int64_t n,
+                                       const uint16_t* w1, const uint16_t* w3, int d, int h,
+                                       const float* eta, int64_t eta_ld, uint16_t* gab,
+                                       int64_t ldab, uint16_t* e, int64_t lde, hipStream_t st);
 hipError_t launch_wide_reduce(const float* part, int splits, int heads, int d, int h,
                               const float* w1, const float* w2, const float* w3, float* o1,
                               float* o2, float* o3, int renorm, const WSet* out_bf16,
