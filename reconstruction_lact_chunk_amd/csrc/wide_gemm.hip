@@ -16,9 +16,9 @@
 // Tiling: a workgroup of 8 waves owns TM = 256 tokens x TN = 128 hidden units
 // of both W1 and W3 and runs the whole contraction in k-steps of 32.  The
 // products are taken transposed (rows = hidden units, columns = tokens), so
-// each lane's four accumulator rows are four consecutive units of one token: the gate pairs x and b from the same lane
-// and each result leaves as one 8-byte store.  Waves form a 4 x 2 grid over
-// the tile; each holds, per product, 4 x 4 blocks of v_mfma_f32_16x16x32_bf16.
+// each lane's four accumulator rows are four consecutive units of one token:
+// the gate pairs x and b from the same lane.  Waves form a 4 x 2 grid over the
+// tile; each holds, per product, 4 x 4 blocks of v_mfma_f32_16x16x32_bf16.
 //
 // Operands go global -> LDS with the gfx950 direct loads (16 bytes per lane,
 // no register staging) into a ring of four stages: per stage the 256 token
@@ -29,6 +29,12 @@
 // rows x one chunk per 16 lanes) are free of bank conflicts.  One barrier per
 // k-step; fragments of the next k-step are read while the current one's MFMAs
 // run.
+//
+// Measured on this shape: the global -> LDS traffic of the 256 x 256 output
+// tile is what holds the loop below the matrix rate (a copy of the kernel
+// that never refills the ring runs 14 % faster); a fifth stage (160 KB) or
+// two 4-wave workgroups per compute unit are slower, and a larger tile does
+// not fit the registers of 8 waves.
 #include "wide_path.h"
 
 namespace zm {
@@ -53,9 +59,9 @@ struct Shape {
   static constexpr int LDS = STAGES * STAGE;
   static_assert(ROWS % (NW * 16) == 0, "whole loads");
   static_assert(TM / WM == 64 && TN / WN == 64, "64 x 64 units per wave");
-  static_assert(STAGES == 4 && LOADS + 4 < 16, "wait counts");
-  // epilogue: 8 KB of output staging per wave in the last two stages, 4 KB of
-  // the update's e per wave in each of the first two
+  static_assert(STAGES >= 4 && (STAGES - 2) * LOADS + 8 < 64, "wait counts");
+  // epilogue: 4 KB of the update's e per wave in each of two ring buffers, 8 KB
+  // of output staging per wave in two others
   static_assert(NW * 8192 <= 2 * STAGE && NW * 4096 <= STAGE, "epilogue staging");
   static_assert(BLOCKS * LDS <= 160 * 1024, "LDS");
 };
@@ -65,6 +71,25 @@ constexpr int HB = 4, TB = 4;         // 16-unit / 16-token blocks per wave
 enum Mode { kRead = 0, kUpdate = 1 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate: vmcnt(n) (6 bits, split over [3:0] and [15:14]),
+// expcnt untouched, lgkmcnt(0).
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) for an n that is a constant after unrolling.
+__device__ __forceinline__ void wait_vm_lgkm0(int n) {
+  switch (n) {
+#define ZM_WAIT_CASE(N) \
+  case N: __builtin_amdgcn_s_waitcnt(waitcnt_vm(N)); break;
+    ZM_WAIT_CASE(1) ZM_WAIT_CASE(2) ZM_WAIT_CASE(3) ZM_WAIT_CASE(4) ZM_WAIT_CASE(5)
+    ZM_WAIT_CASE(6) ZM_WAIT_CASE(7) ZM_WAIT_CASE(8) ZM_WAIT_CASE(9) ZM_WAIT_CASE(10)
+    ZM_WAIT_CASE(11) ZM_WAIT_CASE(12) ZM_WAIT_CASE(13) ZM_WAIT_CASE(14) ZM_WAIT_CASE(15)
+    ZM_WAIT_CASE(16) ZM_WAIT_CASE(17) ZM_WAIT_CASE(18) ZM_WAIT_CASE(19) ZM_WAIT_CASE(20)
+    ZM_WAIT_CASE(21) ZM_WAIT_CASE(22) ZM_WAIT_CASE(23) ZM_WAIT_CASE(24)
+#undef ZM_WAIT_CASE
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+  }
+}
 
 // Byte offset, inside a stage, of logical 16-byte chunk c of row r.
 __device__ __forceinline__ int swz_off(int r, int c) {
@@ -164,14 +189,17 @@ __global__ __launch_bounds__(S::NW * 64, S::BLOCKS) void k_wide_rows(
           acc[p][hb][tb] = mfma_bf16(f.w[p][hb], f.x[tb], acc[p][hb][tb]);
   };
 
-  // ---- the update's e tile, prefetched during the last k-steps.  Once stage
-  // NK - 4 + hf has been read by every wave (the barrier of k-step
-  // NK - 3 + hf), its ring buffer is free: the wave's rows 32 hf .. 32 hf + 31
-  // of e (its 64 token rows x 64 units) go there by direct loads, 4 KB per
-  // wave, laid out as the staging tiles of the epilogue (row r of 128 bytes,
-  // 16-byte chunk c at slot c ^ (r & 7)).
+  // ---- the update's e tile, prefetched during the last k-steps.  Once there
+  // is no stage left to load, the k-step that would have refilled the buffer
+  // of stage NK - kStages + hf (the barrier of k-step NK - kStages + 1 + hf
+  // has retired every read of it) loads instead the wave's rows 32 hf ..
+  // 32 hf + 31 of e (its 64 token rows x 64 units) there by direct loads, 4 KB
+  // per wave, laid out as the staging tiles of the epilogue (row r of 128
+  // bytes, 16-byte chunk c at slot c ^ (r & 7)).
   const int row0 = (TM / WM) * wm, col0 = (TN / WN) * wn;
-  auto e_tile = [&](int hf) { return smem + ((NK - 4 + hf) % kStages) * kStage + w * 4096; };
+  auto e_tile = [&](int hf) {
+    return smem + ((NK - kStages + hf) % kStages) * kStage + w * 4096;
+  };
   auto load_e = [&](int hf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -184,28 +212,28 @@ __global__ __launch_bounds__(S::NW * 64, S::BLOCKS) void k_wide_rows(
     }
   };
 
-  // ---- pipeline: stages k + 1 .. k + 2 in flight while stage k is read and
-  // k - 1 multiplied.  Direct loads count on vmcnt and complete in order.  Each
-  // wave waits for its own loads of stage k (the loads issued after them may
-  // stay outstanding: kLoads per later stage, 4 per half of the update's e) and
-  // its own LDS reads (the buffer refilled next was read in the previous
-  // iteration); the barrier then makes every wave's part of stage k visible
-  // and every read of that buffer retired, and the workgroup acquire fence on
-  // LDS keeps the next reads below it.  A release fence would also be
+  // ---- pipeline: stages k + 1 .. k + kStages - 2 in flight while stage k is
+  // read and k - 1 multiplied.  Direct loads count on vmcnt and complete in
+  // order.  Each wave waits for its own loads of stage k (the loads issued
+  // after them may stay outstanding: kLoads per later stage, 4 per half of the
+  // update's e) and its own LDS reads (the buffer refilled next was read in
+  // the previous iteration); the barrier then makes every wave's part of stage
+  // k visible and every read of that buffer retired, and the workgroup acquire
+  // fence on LDS keeps the next reads below it.  A release fence would also be
   // correct, but the compiler answers it by draining every direct load, which
   // undoes the prefetch.
-  constexpr int kE = MODE == kUpdate ? 4 : 0;
+  constexpr int kEFirst = NK - kStages + 1;   // k-step that issues e's first half
   auto wait_stage = [&](int k) {
-    if (k + 2 < NK) __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kLoads));
-    else if (k + 1 < NK) __builtin_amdgcn_s_waitcnt(0x0070 | (kLoads + kE));
-    else __builtin_amdgcn_s_waitcnt(0x0070 | (2 * kE));
+    const int later = (kStages - 2 < NK - 1 - k ? kStages - 2 : NK - 1 - k) * kLoads;
+    const int halves = MODE != kUpdate ? 0 : (k - kEFirst < 0 ? 0 : (k - kEFirst > 2 ? 2 : k - kEFirst));
+    wait_vm_lgkm0(later + 4 * halves);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
   };
   auto issue = [&](int k) {   // the loads that follow the wait of k-step k
     if (k + kStages - 1 < NK) load_stage(k + kStages - 1);
-    else if (MODE == kUpdate && k == NK - 3) load_e(0);
-    else if (MODE == kUpdate && k == NK - 2) load_e(1);
+    else if (MODE == kUpdate && k == kEFirst) load_e(0);
+    else if (MODE == kUpdate && k == kEFirst + 1) load_e(1);
   };
 #pragma unroll
   for (int k = 0; k < kStages - 1; ++k) load_stage(k);
@@ -213,6 +241,7 @@ __global__ __launch_bounds__(S::NW * 64, S::BLOCKS) void k_wide_rows(
   wait_stage(0);
   issue(0);
   read_frags(0, fa);
+#pragma unroll   // fully: every wait count and ring offset is then a constant
   for (int k = 1; k < NK; k += 2) {
     wait_stage(k);
     issue(k);
@@ -240,7 +269,9 @@ __global__ __launch_bounds__(S::NW * 64, S::BLOCKS) void k_wide_rows(
   // scheduling region (mixed in, its addresses are computed early and spilled).
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();   // every wave is done with the ring; the e loads have landed
-  unsigned char* out_tile = smem + 2 * kStage + w * 8192;   // output staging rows
+  // output staging: two ring buffers other than e's, 4 waves in each
+  unsigned char* out_tile =
+      smem + ((NK + 2 + w / 4) % kStages) * kStage + (w % 4) * 8192;
   auto out_row = [&](int r) { return out_tile + r * 128; };
   auto e_row = [&](int r) { return e_tile(r >> 5) + (r & 31) * 128; };
   auto frag_at = [&](auto row, int tb, int hb) {   // this lane's 8 bytes of block (tb, hb)
