@@ -67,6 +67,8 @@ struct Shape {
 };
 using Cfg = Shape<256, 4, 4, 1>;   // 8 waves, 128 KB: one workgroup per CU
 constexpr int HB = 4, TB = 4;         // 16-unit / 16-token blocks per wave
+constexpr int kHidGroups = 4;         // XCD groups over the hidden tiles (a divisor of 8; 4
+                                      // measured best: each token tile is fetched by 2 XCDs)
 
 enum Mode { kRead = 0, kUpdate = 1 };
 
@@ -112,15 +114,17 @@ __global__ __launch_bounds__(S::NW * 64, S::BLOCKS) void k_wide_rows(
   constexpr int kLoads = S::LOADS;
   __shared__ __attribute__((aligned(16))) unsigned char smem[S::LDS];
 
-  // Block -> tile: the 8 XCDs take blocks round-robin; XCD x owns the hidden
-  // tiles x * per_xcd .. (their weight rows stay in its L2; the launchers
-  // require a multiple of 8 tiles) and walks the token tiles, its hidden
-  // tiles of one token tile next to each other.
-  const int per_xcd = ncols / TN / 8;
+  // Block -> tile: the 8 XCDs take blocks round-robin.  They form kHidGroups
+  // groups of hidden tiles x 8 / kHidGroups groups of token tiles: XCD x owns
+  // hidden tiles (x % kHidGroups) * per_xcd .. (their weight rows stay in its
+  // L2) and the token tiles t with t % (8 / kHidGroups) == x / kHidGroups,
+  // its hidden tiles of one token tile next to each other.
+  constexpr int kTokGroups = 8 / kHidGroups;
+  const int per_xcd = ncols / TN / kHidGroups;
   const int b = blockIdx.x;
   const int xcd = b & 7, i = b >> 3;
-  const int ht = xcd * per_xcd + i % per_xcd;
-  const int64_t t0 = (int64_t)(i / per_xcd) * TM;
+  const int ht = (xcd % kHidGroups) * per_xcd + i % per_xcd;
+  const int64_t t0 = ((int64_t)(i / per_xcd) * kTokGroups + xcd / kHidGroups) * TM;
   if (t0 >= n) return;
   const int j0 = ht * TN;
 
@@ -374,7 +378,10 @@ namespace {
 
 // One block per (token tile, hidden tile).
 template <class S>
-unsigned rows_grid(int64_t n, int ncols) { return (unsigned)(ceil_div(n, S::TM) * (ncols / TN)); }
+unsigned rows_grid(int64_t n, int ncols) {
+  constexpr int kTokGroups = 8 / kHidGroups;
+  return (unsigned)(ceil_div(ceil_div(n, S::TM), kTokGroups) * kTokGroups * (ncols / TN));
+}
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
