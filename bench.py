@@ -509,9 +509,11 @@ def main():
             kern[nm] = {"avg_ms": round(avg[nm], 4), "achieved_tflops": round(ach, 1),
                         "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
         if wide:
-            for nm in ("update", "apply"):
-                kern[nm]["what"] = ("per 131,072-token block: hipBLASLt GEMMs (bf16, fp32 "
-                                    "accumulation) and the wide gate kernel")
+            kern["update"]["what"] = ("per 131,072-token block: e = W2^T v (hipBLASLt), the W1 / W3 "
+                                      "products with the gate backward in their epilogue "
+                                      "(k_wide_rows), the reduction products (hipBLASLt)")
+            kern["apply"]["what"] = ("per 131,072-token block: the W1 / W3 products with the gate in "
+                                     "their epilogue (k_wide_rows), O = U' W2'^T (hipBLASLt)")
         kern["cast"] = {"avg_ms": round(avg["cast"], 4)}
         kern["reduce"] = {"avg_ms": round(avg["reduce"], 4)}
         if whole:
