@@ -159,6 +159,22 @@ ZM_API int zm_ttt_update(const zm_ttt_desc* desc, int64_t n_kv,
                   float* w1_out, float* w2_out, float* w3_out,
                   void* workspace, size_t workspace_bytes, void* stream);
 
+/* Update and its virtual loss (review Eq. (2)): as zm_ttt_update, and
+ * loss[h] = sum_{i<n_kv} eta_i L(f_W(k_i), v_i) = -sum_i eta_i f_W(k_i)^T v_i
+ * of head h at the incoming W (the loss whose gradient the step follows).
+ * It is read from the update's own registers: f^T v = u . (W2^T v) with
+ * u = SiLU(W1 k) (*) W3 k and W2^T v both formed for the gradient, so the
+ * loss costs one multiply-add per (token, hidden unit) and a fixed-order
+ * sum.  loss: device pointer to heads floats (fp32; operands as the update's
+ * bf16 ones).  n_kv = 0 writes zeros.  Bitwise reproducible; W_hat is
+ * bitwise that of zm_ttt_update.  The bf16 narrow heads only: fp32 io and the
+ * full-width shape return ZM_ERR_UNSUPPORTED.  Workspace as zm_ttt_update. */
+ZM_API int zm_ttt_update_loss(const zm_ttt_desc* desc, int64_t n_kv,
+                  const void* k, const void* v, const float* eta,
+                  const float* w1, const float* w2, const float* w3,
+                  float* w1_out, float* w2_out, float* w3_out, float* loss,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 /* Apply (review Eq. (4)): o_i = f_W(q_i) for i < n_q, per head.
  * q, o: [n_q, heads, d_head] in desc->io_dtype; o must not overlap q. */
 ZM_API int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q,

@@ -23,8 +23,8 @@ SCRATCH_BYTES = 64 << 20  # ZM_TTT_SCRATCH_BYTES
 STEP_GRADIENT, STEP_NEWTON_SCHULZ = 0, 1
 
 EXPORTED = (
-    "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-    "zm_ttt_update_apply_scratch",
+    "zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_update_loss", "zm_ttt_apply",
+    "zm_ttt_update_apply", "zm_ttt_update_apply_scratch",
     "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size", "zm_ttt_layer",
     "zm_status_string", "zm_ttt_last_error", "zm_ttt_version", "zm_ttt_set_profile_events",
 )
@@ -79,6 +79,8 @@ def load_library(path: str | None = None):
     lib = ctypes.CDLL(p)
     lib.zm_ttt_workspace_size.argtypes = [_DESC, _I64, _I64, ctypes.POINTER(_SZ)]
     lib.zm_ttt_update.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]
+    lib.zm_ttt_update_loss.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                       _SZ, _P]
     lib.zm_ttt_apply.argtypes = [_DESC, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]
     lib.zm_ttt_update_apply.argtypes = [_DESC, _I64, _P, _P, _P, _I64, _P, _P, _P, _P, _P, _P, _P,
                                         _P, _P, _SZ, _P]
@@ -98,8 +100,8 @@ def load_library(path: str | None = None):
     lib.zm_ttt_last_error.restype = ctypes.c_char_p
     lib.zm_ttt_version.argtypes = []
     lib.zm_ttt_set_profile_events.argtypes = [ctypes.POINTER(_P), ctypes.c_int]
-    for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_apply", "zm_ttt_update_apply",
-                 "zm_ttt_update_apply_scratch",
+    for name in ("zm_ttt_workspace_size", "zm_ttt_update", "zm_ttt_update_loss", "zm_ttt_apply",
+                 "zm_ttt_update_apply", "zm_ttt_update_apply_scratch",
                  "zm_ttt_stream_step", "zm_ttt_chunked", "zm_ttt_layer_workspace_size",
                  "zm_ttt_layer", "zm_ttt_version", "zm_ttt_set_profile_events"):
         getattr(lib, name).restype = ctypes.c_int
@@ -274,6 +276,32 @@ def update(k, v, eta, w1, w2, w3, renorm=False, out=None, workspace=None,
                                       _ws_bytes(ws), _stream(w1.device))
     _check(st, "zm_ttt_update")
     return outs
+
+
+def update_loss(k, v, eta, w1, w2, w3, renorm=False, out=None, loss=None, workspace=None,
+                step_rule=STEP_GRADIENT):
+    """The update of `update` and its virtual loss at the incoming W:
+    loss[h] = -sum_i eta_i f_W(k_i) . v_i per head (fp32, [H]), read from the
+    update's registers.  Returns ((W1_hat, W2_hat, W3_hat), loss).  bf16
+    narrow heads only."""
+    io = _io_of(k, v)
+    n = k.shape[0]
+    desc = make_desc(w1, w2, w3, io, renorm, k, v, step_rule=step_rule, rows=[n, n],
+                     check_device=False)
+    _eta(eta, n, desc.heads)
+    outs = out if out is not None else tuple(torch.empty_like(w) for w in (w1, w2, w3))
+    _check_out_weights(outs, w1, w2, w3)
+    if loss is None:
+        loss = torch.empty(desc.heads, dtype=torch.float32, device=w1.device)
+    if loss.dtype != torch.float32 or loss.numel() != desc.heads or not loss.is_contiguous():
+        raise ZmError(f"loss must be a contiguous fp32 tensor of {desc.heads} elements")
+    _on_gpu(k, v, eta, w1, w2, w3, *outs, loss)
+    ws, _ = _workspace(desc, n, 0, w1.device, workspace)
+    st = load_library().zm_ttt_update_loss(ctypes.byref(desc), n, _ptr(k), _ptr(v), _ptr(eta),
+                                           _ptr(w1), _ptr(w2), _ptr(w3), *map(_ptr, outs),
+                                           _ptr(loss), _ptr(ws), _ws_bytes(ws), _stream(w1.device))
+    _check(st, "zm_ttt_update_loss")
+    return outs, loss
 
 
 def apply(q, w1, w2, w3, out=None, workspace=None):

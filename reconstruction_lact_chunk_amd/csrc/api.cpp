@@ -34,7 +34,7 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10200;  // 1.2.0
+constexpr int kVersion = 10300;  // 1.3.0
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
@@ -101,14 +101,14 @@ struct Ws {
 };
 
 struct Layout {
-  size_t set_a, set_b, part, total;
+  size_t set_a, set_b, part, loss, total;   // loss: virtual-loss block sums (narrow heads)
   UpdatePlan plan;
 };
 
 // Workspace: two bf16 weight sets (4 arrays each), then the partial sums (or,
 // for the full width, the token-block buffers and the partial sums).
 Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
-  Layout L;
+  Layout L{};
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const size_t set_bytes = round_up(4 * welems * sizeof(uint16_t), 256);
   L.set_a = 0;
@@ -121,9 +121,12 @@ Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
     return L;
   }
   L.plan = plan_update(n_kv, d->heads, d->d_hidden);
-  // slots for any update of at most n_kv tokens (see update_slots)
+  // slots for any update of at most n_kv tokens (see update_slots), then one
+  // float per update workgroup for the virtual loss
   const int slots = update_slots(n_kv, d->heads, d->d_hidden);
-  L.total = L.part + round_up((size_t)slots * 3 * welems * sizeof(float), 256);
+  const int nsl = d->d_hidden / kHidPerWg > 0 ? d->d_hidden / kHidPerWg : 1;
+  L.loss = L.part + round_up((size_t)slots * 3 * welems * sizeof(float), 256);
+  L.total = L.loss + round_up((size_t)slots * d->heads * nsl * sizeof(float), 256);
   return L;
 }
 
@@ -212,7 +215,8 @@ int finish_update(const zm_ttt_desc* d, int64_t n, const float* w1, const float*
 // emit is non-null the reduce also writes the bf16 copies of W_hat there.
 int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, const float* eta,
                const float* w1, const float* w2, const float* w3, float* o1, float* o2,
-               float* o3, Ws wsp, const WSet* emit, bool cast_done, hipStream_t st) {
+               float* o3, Ws wsp, const WSet* emit, bool cast_done, hipStream_t st,
+               float* loss = nullptr) {
   void* const ws = wsp.p;
   const Layout L = layout(d, n, 0);
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
@@ -246,6 +250,8 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
   }
   float* part = (float*)((char*)ws + L.part);
   ZM_TRY(check_part_range(L.part, L.plan.splits, welems, wsp.bytes));
+  // the virtual loss's block sums (bf16 narrow path only; the entry point checks)
+  float* const loss_part = loss ? (float*)((char*)ws + L.loss) : nullptr;
   if (n > 0) {
     if (d->io_dtype == ZM_BF16) {
       if (!cast_done) {
@@ -254,13 +260,15 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
       }
       Scoped s(kStageUpdate, st);
       ZM_HIP(launch_update_bf16((const uint16_t*)k, (const uint16_t*)v, eta, n, d->ld_tok,
-                                d->heads, d->d_head, d->d_hidden, a, part, L.plan, st));
+                                d->heads, d->d_head, d->d_hidden, a, part, L.plan, st, loss_part));
     } else {
       Scoped s(kStageUpdate, st);
       ZM_HIP(launch_update_f32((const float*)k, (const float*)v, eta, n, d->ld_tok, d->heads,
                                d->d_head, d->d_hidden, w1, w2, w3, part, L.plan, st));
     }
   }
+  if (loss)  // n = 0: zeros
+    ZM_HIP(launch_loss_sum(loss_part, n > 0 ? L.plan.splits : 0, d->heads, d->d_hidden, loss, st));
   return finish_update(d, n, w1, w2, w3, o1, o2, o3, part, L.plan.splits, emit, st);
 }
 
@@ -588,6 +596,28 @@ int zm_ttt_update(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const vo
   hipStream_t st = (hipStream_t)stream;
   return run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out,
                     Ws{workspace, workspace_bytes}, nullptr, false, st);
+}
+
+int zm_ttt_update_loss(const zm_ttt_desc* desc, int64_t n_kv, const void* k, const void* v,
+                       const float* eta, const float* w1, const float* w2, const float* w3,
+                       float* w1_out, float* w2_out, float* w3_out, float* loss, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  ZM_TRY(check_desc(desc));
+  if (is_wide(desc) || desc->io_dtype != ZM_BF16) {
+    set_last_error("the virtual loss is computed by the bf16 narrow-head update only");
+    return ZM_ERR_UNSUPPORTED;
+  }
+  if (loss == nullptr || !aligned(loss, 4)) return ZM_ERR_INVALID_ARG;
+  ZM_TRY(check_counts(n_kv, 0));
+  ZM_TRY(check_tokens(k, n_kv));
+  ZM_TRY(check_tokens(v, n_kv));
+  ZM_TRY(check_eta(eta, n_kv));
+  ZM_TRY(check_weights(w1, w2, w3));
+  ZM_TRY(check_weights(w1_out, w2_out, w3_out));
+  ZM_TRY(check_ws(desc, n_kv, 0, workspace, workspace_bytes));
+  hipStream_t st = (hipStream_t)stream;
+  return run_update(desc, n_kv, k, v, eta, w1, w2, w3, w1_out, w2_out, w3_out,
+                    Ws{workspace, workspace_bytes}, nullptr, false, st, loss);
 }
 
 int zm_ttt_apply(const zm_ttt_desc* desc, int64_t n_q, const void* q, const float* w1,

@@ -101,12 +101,19 @@ __device__ __forceinline__ void gate_backward(float x, float b, float e, float& 
 // The work of update block `blk` (one workgroup of 512 threads): the kernels
 // that run it pass their block index (offset so that blk % 8 is still the
 // block's XCD) and a 16-byte-aligned LDS buffer of UpdCfg::LDS_ELEMS elements.
-template <int D, int HID>
+// With LOSS, the block also sums u' . e over its tokens and hidden units (u'
+// = -log2(e) u and e = W2^T (eta v) are both in registers for the gate
+// backward) and writes the sum to loss_part[(chunk * heads + head) * NSL +
+// slice]: the per-token loss -eta_i f(k_i)^T v_i = -eta_i u_i . W2^T v_i of
+// the review of ZipMap, Method 2, Eq. (2), summed, is ln(2) times the sum of
+// those block values.
+template <int D, int HID, bool LOSS = false>
 __device__ __forceinline__ void update_tiles(
     int blk, uint16_t* __restrict__ lds, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const float* __restrict__ eta, int64_t n, int64_t ld,
     int heads, const uint16_t* __restrict__ w1b, const uint16_t* __restrict__ w3b,
-    const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk) {
+    const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk,
+    float* __restrict__ loss_part = nullptr) {
   using C = UpdCfg<D, HID>;
   constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT;
 
@@ -146,6 +153,7 @@ __device__ __forceinline__ void update_tiles(
     acc3[m] = acc1[m];
     acc2[m] = acc1[m];
   }
+  float lacc = 0.f;   // LOSS: this lane's sum of u' e
 
   // ---- staging: one 16-byte chunk of k and of v per thread ---------------
   const bool has_item = tid < C::ITEMS;
@@ -238,6 +246,10 @@ __device__ __forceinline__ void update_tiles(
         float ga0, gb0, u0, ga1, gb1, u1;
         gate_backward(f.a[mb][i], f.b[mb][i], f.e[mb][i], ga0, gb0, u0);
         gate_backward(f.a[mb][i + 1], f.b[mb][i + 1], f.e[mb][i + 1], ga1, gb1, u1);
+        if constexpr (LOSS) {
+          lacc = fmaf(u0, f.e[mb][i], lacc);
+          lacc = fmaf(u1, f.e[mb][i + 1], lacc);
+        }
         gap[2 * mb + i / 2] = pack_bf16x2(ga0, ga1);
         gbp[2 * mb + i / 2] = pack_bf16x2(gb0, gb1);
         up[2 * mb + i / 2] = pack_bf16x2(u0, u1);
@@ -375,6 +387,10 @@ __device__ __forceinline__ void update_tiles(
           unsigned pu = pack_bf16x2(g_u[0], g_u[1]);
           pin(pu);
           up[pr] = pu;
+          if constexpr (LOSS) {
+            el(0, [&](int, float, float, float e) { lacc = fmaf(g_u[0], e, lacc); });
+            el(1, [&](int, float, float, float e) { lacc = fmaf(g_u[1], e, lacc); });
+          }
           break;
         }
       }
@@ -446,6 +462,21 @@ __device__ __forceinline__ void update_tiles(
       ga_ = cur;
     }
     backward(ntiles - 1, ga_);
+  }
+  if constexpr (LOSS) {
+    // lanes in butterfly order, then the 8 wave sums in wave order (fixed)
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) lacc += __shfl_xor(lacc, m, 64);
+    __syncthreads();   // the tile ring is no longer read
+    float* red = (float*)lds;
+    if (l == 0) red[w] = lacc;
+    __syncthreads();
+    if (tid == 0) {
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) sum += red[i];
+      loss_part[((int64_t)chunk_id * heads + head) * C::NSL + slice] = sum;
+    }
   }
   // all three partial sums were accumulated from ga', gb', u', which carry -log2(e)
 #pragma unroll

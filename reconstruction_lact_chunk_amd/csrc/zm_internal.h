@@ -163,9 +163,15 @@ inline ApplyPlan plan_apply(int64_t n, int heads, int64_t wgs = kTargetWgs) {
 hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int heads, int d, int h,
                        WSet out, hipStream_t st);
 
+// loss_part non-null: also the virtual loss's per-workgroup sums (splits x
+// heads x h / kHidPerWg floats) for launch_loss_sum.
 hipError_t launch_update_bf16(const uint16_t* k, const uint16_t* v, const float* eta, int64_t n,
                               int64_t ld, int heads, int d, int h, WSet w, float* part,
-                              UpdatePlan plan, hipStream_t st);
+                              UpdatePlan plan, hipStream_t st, float* loss_part = nullptr);
+// loss[head] from the per-workgroup sums of launch_update_bf16 (splits may be
+// 0: zeros).
+hipError_t launch_loss_sum(const float* loss_part, int splits, int heads, int h, float* loss,
+                           hipStream_t st);
 
 hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
                          const float* w1, const float* w2, const float* w3,

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10200
+    assert zm.version() == 10300
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -67,8 +67,11 @@ def test_workspace_size_structure():
     assert base == 2 * 4 * welems * 2        # two bf16 weight sets, no partial sums
     st, big = ws_size(de, 961_800, 961_800)
     assert st == 0
+    # the partial-sum slots (3 h d fp32 per head each), then one fp32 per
+    # update workgroup (heads x h / 128 per slot) for the virtual loss,
+    # rounded up to 256 bytes
     parts = (big - base) // (3 * welems * 4)
-    assert (big - base) % (3 * welems * 4) == 0
+    assert big == base + parts * 3 * welems * 4 + (parts * 8 * 2 * 4 + 255) // 256 * 256
     assert 1 <= parts <= 256
     # more tokens never need fewer partial sums; queries need no workspace
     sizes = [ws_size(de, n, 0)[1] for n in (1, 31, 32, 33, 1000, 10_992, 137_400, 961_800)]
@@ -187,6 +190,31 @@ ODD = P((1 << 20) + 2)  # misaligned for every check
 def call_update(de, n, k=GOOD, v=GOOD, eta=GOOD, w=(GOOD, GOOD, GOOD), wo=(GOOD, GOOD, GOOD),
                 ws=GOOD, ws_bytes=0):
     return lib().zm_ttt_update(ctypes.byref(de), n, k, v, eta, *w, *wo, ws, ws_bytes, None)
+
+
+def call_update_loss(de, n, loss=GOOD, k=GOOD, ws_bytes=0):
+    return lib().zm_ttt_update_loss(None if de is None else ctypes.byref(de), n, k, GOOD, GOOD,
+                                    GOOD, GOOD, GOOD, GOOD, GOOD, GOOD, loss, GOOD, ws_bytes, None)
+
+
+def test_update_loss_rejects_before_any_hip_call():
+    de = desc()
+    need = ws_size(de, 100, 0)[1]
+    # only the bf16 narrow-head update carries the loss
+    assert call_update_loss(desc(io=zm.F32), 100, ws_bytes=need) == zm.ERR_UNSUPPORTED
+    wd = desc(heads=1, d=1024, h=2048)
+    assert call_update_loss(wd, 100, ws_bytes=ws_size(wd, 100, 0)[1]) == zm.ERR_UNSUPPORTED
+    assert "bf16 narrow-head" in zm.last_error()
+    # a null or misaligned loss pointer, then the update's own checks
+    assert call_update_loss(de, 100, loss=None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update_loss(de, 100, loss=P((1 << 20) + 2), ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update_loss(de, 100, k=None, ws_bytes=need) == zm.ERR_INVALID_ARG
+    assert call_update_loss(de, 100, ws_bytes=need - 1) == zm.ERR_WORKSPACE
+    assert call_update_loss(None, 100, ws_bytes=need) == zm.ERR_INVALID_ARG
+    with pytest.raises(zm.ZmError, match="fp32 tensor"):
+        w1, w2 = torch.zeros(1, 128, 64), torch.zeros(1, 64, 128)
+        zm.update_loss(*[torch.zeros(3, 1, 64, dtype=torch.bfloat16)] * 2, torch.zeros(3, 1),
+                       w1, w2, w1.clone(), loss=torch.zeros(2))
 
 
 def test_update_rejects_bad_pointers_before_any_hip_call():
