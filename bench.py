@@ -66,7 +66,7 @@ def parse():
                         "launch overhead per call)")
     p.add_argument("--no-configs", action="store_true",
                    help="with the default f700 workload, skip the other configurations (tiny, "
-                        "f8, f100 + target view, stream256, f700x24) timed after it")
+                        "f8, f100 + target view, stream256, f700x24, fw700) timed after it")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="first run one plain device copy of this many MiB (a known-size "
                         "reference dispatch for scaling HBM counters)")
@@ -154,9 +154,10 @@ def cpu_baseline_layer(xs, w_in, w_gate, gamma, w, sample_tokens, renorm, step_r
 
 # Configurations reported beside the headline, each in its own timed region:
 # (name, timed steps, warm-up steps).  A stream256 step is 256 frames, an
-# f700x24 step 24 layers.
+# f700x24 step 24 layers; fw700 is the same 961,800 tokens through the one
+# full-width head (d 1024, hidden 2048).
 EXTRA_CONFIGS = (("tiny", 200, 20), ("f8", 100, 10), ("f100", 30, 5), ("stream256", 3, 1),
-                 ("f700x24", 2, 1))
+                 ("f700x24", 2, 1), ("fw700", 3, 1))
 
 
 def time_region(torch, stream, fn, steps, warmup):

@@ -41,7 +41,7 @@ def test_stored_traffic_follows_the_kernel_source_hash_and_workload(monkeypatch)
 
 def test_extra_configs_cover_every_configuration():
     names = [c[0] for c in bench.EXTRA_CONFIGS]
-    assert set(names) == {"tiny", "f8", "f100", "stream256", "f700x24"}
+    assert set(names) == {"tiny", "f8", "f100", "stream256", "f700x24", "fw700"}
     for name, steps, warmup in bench.EXTRA_CONFIGS:
         assert name in WL.WORKLOADS and steps >= 1 and warmup >= 1
 
