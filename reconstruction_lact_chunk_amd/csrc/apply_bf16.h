@@ -125,18 +125,14 @@ __device__ __forceinline__ void apply_tiles(
   // Query rows past the end are fetched from a valid row (the tile's first)
   // and their outputs are never stored, so no zeroing is needed.
   const int lane_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
-  u32x4 qr = {0u, 0u, 0u, 0u};
   auto fetch = [&](int it) {
     const int64_t t0 = t_begin + (int64_t)it * T;
-    if (t0 + T <= t_end) {
-      qr = *(const u32x4*)(qp + t0 * ld + lane_off);
-    } else {
-      const int64_t tc = (has_item && t0 < t_end && t0 + s_tok < t_end) ? t0 + s_tok
-                         : (t0 < t_end ? t0 : t_begin);
-      qr = *(const u32x4*)(qp + tc * ld + head * D + (has_item ? 8 * s_ch : 0));
-    }
+    if (t0 + T <= t_end) return *(const u32x4*)(qp + t0 * ld + lane_off);
+    const int64_t tc = (has_item && t0 < t_end && t0 + s_tok < t_end) ? t0 + s_tok
+                       : (t0 < t_end ? t0 : t_begin);
+    return *(const u32x4*)(qp + tc * ld + head * D + (has_item ? 8 * s_ch : 0));
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, const u32x4& qr) {
     if constexpr (C::ITEMS < kWaves * 64) {
       if (!has_item) return;
     }
@@ -287,10 +283,11 @@ __device__ __forceinline__ void apply_tiles(
   constexpr int NS2 = TBW * KS2 / 2;   // phase-2 slots
   constexpr int NS1 = KS1 * NB;        // phase-1 slots
   constexpr int NSLOT = NS1 + NS2;
-  fetch(0);
-  stage(0);
-  fetch(1);
-  stage(1);
+  // The prologue's three tiles are fetched together, so that their memory
+  // round trips overlap.
+  const u32x4 q0 = fetch(0), q1 = fetch(1), q2 = fetch(2);
+  stage(0, q0);
+  stage(1, q1);
   __syncthreads();
   Acc1 cur = phase1(0);
   __syncthreads();  // every wave is done with Q(0) before Q(2) reuses its buffer
@@ -300,8 +297,7 @@ __device__ __forceinline__ void apply_tiles(
     gate_all(cur, upk);
     if (ntiles > 1) cur = phase1(1);
     write_u(0, upk);
-    fetch(2);
-    stage(2);
+    stage(2, q2);
     __syncthreads();
   }
   // Slots alternate phase 2 (two MFMAs) and phase 1 (2 * MB1 MFMAs) while
@@ -323,7 +319,7 @@ __device__ __forceinline__ void apply_tiles(
   // shadow of one MFMA.
   constexpr int NMICRO = (NE / 4) * 15;
   auto step = [&](int it, const Acc1& cur, Acc1& nxt) __attribute__((always_inline)) {
-    fetch(it + 2);
+    const u32x4 qn = fetch(it + 2);
     Frag2 f2[NSLOT];
     bf16x8 f1[NSLOT];
     auto load_slot = [&](int j) {
@@ -414,7 +410,7 @@ __device__ __forceinline__ void apply_tiles(
       if (m >= mi) micro(m);
     write_u(it, upk);
     o_to_lds(acc2, it - 1);
-    stage(it + 2);
+    stage(it + 2, qn);
     // Output tile it - 2 (in LDS since the previous iteration) leaves last,
     // so that its store has a whole iteration to complete before the next
     // wait on the memory counter.

@@ -342,9 +342,7 @@ __global__ __launch_bounds__(256) void k_sum_splits(float* __restrict__ part, in
                                                     int64_t slot) {
   const int64_t e = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (e >= slot) return;
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int si = 0; si < splits; ++si) sum += *(const f32x4*)(part + si * slot + e);
-  *(f32x4*)(part + e) = sum;
+  *(f32x4*)(part + e) = sum_slots(part + e, slot, splits);
 }
 
 template <int D, int HID>

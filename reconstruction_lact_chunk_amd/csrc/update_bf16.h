@@ -158,18 +158,21 @@ __device__ __forceinline__ void update_tiles(
   // ---- staging: one 16-byte chunk of k and of v per thread ---------------
   const bool has_item = tid < C::ITEMS;
   const int s_tok = tid / CPT, s_ch = tid - (tid / CPT) * CPT;
-  u32x4 kr = {0u, 0u, 0u, 0u}, vr = {0u, 0u, 0u, 0u};
-  float er = 0.f;
+  struct Staged {
+    u32x4 k, v;
+    float e;
+  };
   // Per-lane element offsets of this thread's staging chunk inside a tile;
   // the tile base is uniform, so loads use a scalar base + vector offset.
   const int lane_tok_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
   const int lane_eta_off = (has_item ? s_tok : 0) * heads + head;
   auto fetch = [&](int it) {
     const int64_t t0 = t_begin + (int64_t)it * T;
+    Staged r;
     if (t0 + T <= t_end) {  // whole tile in range (uniform branch)
-      kr = *(const u32x4*)(kp + t0 * ld + lane_tok_off);
-      vr = *(const u32x4*)(vp + t0 * ld + lane_tok_off);
-      er = eta[t0 * heads + lane_eta_off];
+      r.k = *(const u32x4*)(kp + t0 * ld + lane_tok_off);
+      r.v = *(const u32x4*)(vp + t0 * ld + lane_tok_off);
+      r.e = eta[t0 * heads + lane_eta_off];
     } else {
       // Tail tile: out-of-range tokens get eta = 0 and a real token's k and v
       // (finite values; eta = 0 zeroes their contribution, since e, ga, gb
@@ -179,13 +182,14 @@ __device__ __forceinline__ void update_tiles(
       const bool ok = has_item && t0 + s_tok < t_end;
       const int64_t tc = ok ? t0 + s_tok : (t0 < t_end ? t0 : t_begin);
       const int col = has_item ? 8 * s_ch : 0;
-      kr = *(const u32x4*)(kp + tc * ld + head * D + col);
-      vr = *(const u32x4*)(vp + tc * ld + head * D + col);
+      r.k = *(const u32x4*)(kp + tc * ld + head * D + col);
+      r.v = *(const u32x4*)(vp + tc * ld + head * D + col);
       const float e0 = eta[tc * heads + head];
-      er = ok ? e0 : 0.f;
+      r.e = ok ? e0 : 0.f;
     }
+    return r;
   };
-  auto stage = [&](int buf) {
+  auto stage = [&](int buf, const Staged& r) {
     if constexpr (C::ITEMS < kWaves * 64) {
       if (!has_item) return;
     }
@@ -193,9 +197,9 @@ __device__ __forceinline__ void update_tiles(
     uint16_t* vtm = ktm + C::TILE;
     u32x4 vs;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(vr[q]) * er, bf16hi(vr[q]) * er);
+    for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(r.v[q]) * r.e, bf16hi(r.v[q]) * r.e);
     const int off = tile_off<D>(s_tok, 8 * s_ch);
-    *(u32x4*)(ktm + off) = kr;
+    *(u32x4*)(ktm + off) = r.k;
     *(u32x4*)(vtm + off) = vs;
   };
 
@@ -319,7 +323,7 @@ __device__ __forceinline__ void update_tiles(
   constexpr int NMICRO = 4 * 13;
   auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur, bool barrier)
       __attribute__((always_inline)) {
-    fetch(t + 3);
+    const Staged nx = fetch(t + 3);
     Frag2 fr[NSLOT];
 #pragma unroll
     for (int j = 0; j < LA; ++j) fr[j] = load_slot(t, j);
@@ -420,7 +424,7 @@ __device__ __forceinline__ void update_tiles(
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 3 * NSLOT; i < NMICRO; ++i) micro(i);
-    stage(t + 3);
+    stage(t + 3, nx);
     if (barrier) __syncthreads();
     cur = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
   };
@@ -430,20 +434,20 @@ __device__ __forceinline__ void update_tiles(
   // t + 1.  A barrier closes every even iteration only: a staged tile is
   // first read two iterations later, and a buffer is rewritten (NBUF = 8)
   // four iterations after its last read, so a barrier always lies between.
+  // The prologue's four tiles are fetched together, so that their memory
+  // round trips overlap (on a short chunk the prologue is a large part of
+  // the block's time).
   if (ntiles > 0) {
-    fetch(0);
-    stage(0);
-    fetch(1);
-    stage(1);
-    fetch(2);
-    stage(2);
+    const Staged s0 = fetch(0), s1 = fetch(1), s2 = fetch(2), s3 = fetch(3);
+    stage(0, s0);
+    stage(1, s1);
+    stage(2, s2);
     __syncthreads();
     Fwd fa = forward(0), fb;
     Grad ga_ = pointwise(fa), gb_;
     // t = 0: no backward yet
-    fetch(3);
     if (ntiles > 1) fa = forward(1);
-    stage(3);
+    stage(3, s3);
     __syncthreads();
     int t = 1;
     for (; t + 2 < ntiles; t += 2) {  // steady state, two iterations per trip

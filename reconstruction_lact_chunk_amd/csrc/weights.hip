@@ -71,14 +71,13 @@ __device__ __forceinline__ float group_sum(float x) {
 // one wave.  Each thread adds the S partials of its 4 elements in split order
 // (fixed order: bitwise reproducible), forms W' = W + sum, and for renorm
 // scales its row by ||W_row|| / max(||W'_row||, 1e-12) with both norms summed
-// over the row's lane group.  16-byte loads keep all S partial reads in flight.
+// over the row's lane group.
 template <int LEN>
 __device__ __forceinline__ void reduce_row4(const float* __restrict__ part, int splits,
                                             int64_t pstride, int64_t e, const float* win,
                                             float* wout, int renorm, f32x4& nv) {
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-  for (int si = 0; si < splits; ++si) sum += *(const f32x4*)(part + si * pstride + e);
   const f32x4 wv = *(const f32x4*)(win);
+  const f32x4 sum = sum_slots(part + e, pstride, splits);
   nv = wv + sum;
   if (renorm) {
     float so = 0.f, sn = 0.f;

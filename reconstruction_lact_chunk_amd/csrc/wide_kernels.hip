@@ -35,9 +35,8 @@ __device__ __forceinline__ void wide_row(const float* __restrict__ part, int spl
 #pragma unroll
   for (int q = 0; q < EPT; q += 4) {
     const int64_t off = 4 * tid + 1024 * (q / 4);
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int si = 0; si < splits; ++si) sum += *(const f32x4*)(part + si * pstride + e0 + off);
     const f32x4 wv = *(const f32x4*)(win + off);
+    const f32x4 sum = sum_slots(part + e0 + off, pstride, splits);
     const f32x4 n4 = wv + sum;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

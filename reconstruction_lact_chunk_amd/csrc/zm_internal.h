@@ -90,6 +90,27 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
+// p[0] + p[stride] + ... + p[(splits - 1) stride] for 16-byte values, added in
+// slot order from zero (fixed order: bitwise reproducible).  The loads go out
+// in groups of eight before their adds: a plain loop waits for each load
+// before the next add, which makes the partial-sum reduction a chain of
+// dependent memory round trips.
+__device__ __forceinline__ f32x4 sum_slots(const float* __restrict__ p, int64_t stride,
+                                           int splits) {
+  constexpr int G = 8;
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += G) {
+    f32x4 v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (s0 + i < splits) v[i] = *(const f32x4*)(p + (int64_t)(s0 + i) * stride);
+#pragma unroll
+    for (int i = 0; i < G; ++i)
+      if (s0 + i < splits) sum += v[i];
+  }
+  return sum;
+}
+
 // Records a description of the last failure on this thread (read back through
 // zm_ttt_last_error); printf-style.
 void set_last_error(const char* fmt, ...);
