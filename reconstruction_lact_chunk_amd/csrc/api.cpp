@@ -226,7 +226,7 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
     const WideBufs wb = wide_bufs(ws, wsp.bytes, L.part, d->heads, d->d_head, d->d_hidden, n, 0,
                                   ns);
     ZM_TRY(check_wide_bufs(wb, wsp.bytes));
-    int splits = L.plan.splits;
+    const int splits = L.plan.splits;
     if (n > 0) {
       if (!cast_done) {
         Scoped s(kStageCast, st);
@@ -236,16 +236,20 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
       ZM_TRY(wide_update(d->heads, d->d_head, d->d_hidden, d->ld_tok, n, (const uint16_t*)k,
                          (const uint16_t*)v, eta, a, wb, st));
     }
+    // The slots are transposed: launch_wide_tsum adds them in slot order into
+    // wb.sum in natural layouts, which the Newton-Schulz step and the reduce
+    // read as a single slot.
     if (n > 0 && ns) {
       Scoped s(kStageNewtonSchulz, st);
-      ZM_HIP(launch_sum_splits(wb.part, splits, d->heads, d->d_head, d->d_hidden, st));
-      ZM_TRY(wide_newton_schulz(wb.part, d->heads, d->d_head, d->d_hidden, wb.ns, wb.lt_ws,
+      ZM_HIP(launch_wide_tsum(wb.part, splits, d->heads, d->d_head, d->d_hidden, wb.sum, st));
+      ZM_TRY(wide_newton_schulz(wb.sum, d->heads, d->d_head, d->d_hidden, wb.ns, wb.lt_ws,
                                 wb.lt_ws_bytes, st));
-      splits = 1;
     }
     Scoped s(kStageReduce, st);
-    ZM_HIP(launch_wide_reduce(wb.part, splits, d->heads, d->d_head, d->d_hidden, w1, w2, w3, o1,
-                              o2, o3, d->renorm, emit, st));
+    if (n > 0 && !ns)
+      ZM_HIP(launch_wide_tsum(wb.part, splits, d->heads, d->d_head, d->d_hidden, wb.sum, st));
+    ZM_HIP(launch_wide_reduce(n > 0 ? wb.sum : wb.part, n > 0 ? 1 : 0, d->heads, d->d_head,
+                              d->d_hidden, w1, w2, w3, o1, o2, o3, d->renorm, emit, st));
     return ZM_OK;
   }
   float* part = (float*)((char*)ws + L.part);

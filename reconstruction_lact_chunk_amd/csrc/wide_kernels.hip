@@ -111,6 +111,75 @@ __global__ __launch_bounds__(256) void k_wide_reduce(const float* __restrict__ p
   }
 }
 
+// The reduction products leave each partial slot transposed: per head, the
+// slot holds [D1; D3]^T as a row-major d x 2h matrix, then D2^T as h x d (the
+// library runs those orientations faster).  This kernel adds the S slots in
+// slot order and writes the sum in the natural layouts, [D1; D3] (2h x d)
+// and D2 (d x h), to sum[heads][3][h d]: one 64 x 64 tile per workgroup,
+// transposed through LDS (row pitch 65: the tile's writes and its transposed
+// reads are both free of bank conflicts).  Tiles 0 .. 2h d / 4096 - 1 of
+// each head belong to the first matrix, the rest to the second.
+template <int D, int HID>
+__global__ __launch_bounds__(256) void k_wide_tsum(const float* __restrict__ part, int splits,
+                                                   int heads, float* __restrict__ sum) {
+  constexpr int64_t HD = (int64_t)HID * D;
+  constexpr int T13 = (D / 64) * (2 * HID / 64);
+  __shared__ float tile[64][65];
+  const int head = blockIdx.y;
+  int t = blockIdx.x;
+  const bool m2 = t >= T13;
+  if (m2) t -= T13;
+  // input matrix R x C (row-major), output C x R
+  const int R = m2 ? HID : D, C = m2 ? D : 2 * HID;
+  const int64_t base = (int64_t)head * 3 * HD + (m2 ? 2 * HD : 0);
+  const int r0 = 64 * (t / (C / 64)), c0 = 64 * (t % (C / 64));
+  const int64_t pstride = (int64_t)heads * 3 * HD;
+  const int tid = threadIdx.x, tr = tid >> 4, tc = 4 * (tid & 15);
+  const float* src = part + base + (int64_t)(r0 + tr) * C + c0 + tc;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // slots in groups of two, four rows each: eight loads in flight, added in
+  // slot order
+  for (int s0 = 0; s0 < splits; s0 += 2) {
+    f32x4 v[2][4];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (s0 + k < splits) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          v[k][i] = *(const f32x4*)(src + (int64_t)(s0 + k) * pstride + (int64_t)16 * i * C);
+      }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (s0 + k < splits) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += v[k][i];
+      }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tile[tr + 16 * i][tc + k] = acc[i][k];
+  __syncthreads();
+  float* dst = sum + base + (int64_t)(c0 + tr) * R + r0 + tc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = tr + 16 * i;
+    *(f32x4*)(dst + (int64_t)16 * i * R) =
+        f32x4{tile[tc][cc], tile[tc + 1][cc], tile[tc + 2][cc], tile[tc + 3][cc]};
+  }
+}
+
+hipError_t launch_wide_tsum(const float* part, int splits, int heads, int d, int h, float* sum,
+                            hipStream_t st) {
+  if (d != 1024 || h != 2048) return hipErrorInvalidValue;
+  const unsigned tiles = (unsigned)((d / 64) * (2 * h / 64) + (h / 64) * (d / 64));
+  hipLaunchKernelGGL((k_wide_tsum<1024, 2048>), dim3(tiles, (unsigned)heads), dim3(256), 0, st,
+                     part, splits, heads, sum);
+  return hipGetLastError();
+}
+
 hipError_t launch_wide_reduce(const float* part, int splits, int heads, int d, int h,
                               const float* w1, const float* w2, const float* w3, float* o1,
                               float* o2, float* o3, int renorm, const WSet* out_bf16,

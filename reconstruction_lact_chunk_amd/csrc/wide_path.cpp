@@ -7,8 +7,9 @@
 //   update: E = V W2                                  (library GEMM, bf16 out)
 //           [Ga Gb], eta U from K W1^T, K W3^T, E and eta: the two products
 //           with the gate backward in their epilogue   (k_wide_rows, update)
-//           D13 = [Ga Gb]^T K, D2 = V^T (eta U)        (library GEMMs, fp32 partials)
-//           then the fixed-order reduce / step / renorm over the blocks;
+//           D13^T = K^T [Ga Gb], D2^T = (eta U)^T V    (library GEMMs, fp32 partials)
+//           then the fixed-order slot sum into natural layouts, and the
+//           reduce / step / renorm;
 //   apply:  U' = -log2(e) SiLU(Q W1^T) (*) Q W3^T: the two products with the
 //           gate in their epilogue                     (k_wide_rows, read)
 //           O = U' W2'^T                               (library GEMM).
@@ -50,9 +51,11 @@ size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool
   const int64_t rows_q = n_q < kWideBlock ? n_q : kWideBlock;
   const int64_t rows = rows_kv > rows_q ? rows_kv : rows_q;
   const size_t bufs = round_up((size_t)rows * 3 * h * sizeof(uint16_t), 256);
-  const size_t part = round_up((size_t)wide_splits(n_kv) * heads * 3 * (size_t)h * d * sizeof(float),
-                               256);
-  return kWideLtWorkspace + (ns ? round_up(wide_ns_bytes(heads, d, h), 256) : 0) + bufs + part;
+  const size_t slot = (size_t)heads * 3 * (size_t)h * d * sizeof(float);
+  const size_t part = round_up((size_t)wide_splits(n_kv) * slot, 256);
+  const size_t sum = n_kv > 0 ? round_up(slot, 256) : 0;
+  return kWideLtWorkspace + (ns ? round_up(wide_ns_bytes(heads, d, h), 256) : 0) + sum + bufs +
+         part;
 }
 
 WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
@@ -63,7 +66,10 @@ WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int
   w.lt_ws_bytes = kWideLtWorkspace;
   const size_t ns_bytes = ns ? round_up(wide_ns_bytes(heads, d, h), 256) : 0;
   w.ns = ns ? p + kWideLtWorkspace : nullptr;
-  w.ab = (uint16_t*)(p + kWideLtWorkspace + ns_bytes);
+  const size_t sum_bytes =
+      n_kv > 0 ? round_up((size_t)heads * 3 * (size_t)h * d * sizeof(float), 256) : 0;
+  w.sum = n_kv > 0 ? (float*)(p + kWideLtWorkspace + ns_bytes) : nullptr;
+  w.ab = (uint16_t*)(p + kWideLtWorkspace + ns_bytes + sum_bytes);
   const size_t part = (size_t)wide_splits(n_kv) * heads * 3 * (size_t)h * d * sizeof(float);
   // partial sums at the end of the workspace, so the token-block buffers can
   // be sized by the larger of the update and apply counts
@@ -72,7 +78,8 @@ WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int
   const int64_t rows_kv = n_kv < kWideBlock ? n_kv : kWideBlock;
   const int64_t rows_q = n_q < kWideBlock ? n_q : kWideBlock;
   const int64_t rows = rows_kv > rows_q ? rows_kv : rows_q;
-  const size_t ab_end = base + kWideLtWorkspace + ns_bytes + (size_t)rows * 3 * h * sizeof(uint16_t);
+  const size_t ab_end =
+      base + kWideLtWorkspace + ns_bytes + sum_bytes + (size_t)rows * 3 * h * sizeof(uint16_t);
   w.fits = part <= ws_bytes && ab_end <= part_off;
   return w;
 }
@@ -106,26 +113,28 @@ int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* 
         set_last_error("wide forward+gate (update) launch: %s", hipGetErrorString(ge));
         return ZM_ERR_HIP;
       }
-      // minus the gradient over this block: [D1; D3] = [Ga Gb]^T K, D2 = V^T (eta U).
-      // The block's tokens go to kWideSub sub-blocks as one batched product,
-      // each adding into its own partial slot (slot i holds sub-block i of
-      // every block, added in block order): enough output tiles to fill the
-      // GPU, and a fixed summation order.
+      // minus the gradient over this block, transposed: [D1; D3]^T = K^T [Ga Gb]
+      // (d x 2h) and D2^T = (eta U)^T V (h x d); the library runs these
+      // orientations faster than [Ga Gb]^T K and V^T (eta U).  The block's
+      // tokens go to kWideSub sub-blocks as one batched product, each adding
+      // into its own partial slot (slot i holds sub-block i of every block,
+      // added in block order): enough output tiles to fill the GPU, and a
+      // fixed summation order.
       const float beta = blk == 0 ? 0.f : 1.f;
       const int64_t sub = len / kWideSub, rest = len - sub * kWideSub;
       if (sub > 0) {
-        if (!rm_tn(2 * h, d, sub, ab, 2 * h, kb, ld, slot, d, true, w, st, kWideSub,
-                   sub * 2 * h, sub * ld, pstride, beta) ||
-            !rm_tn(d, h, sub, vb, ld, e, h, slot + 2 * hd_elems, h, true, w, st, kWideSub,
-                   sub * ld, sub * h, pstride, beta))
+        if (!rm_tn(d, 2 * h, sub, kb, ld, ab, 2 * h, slot, 2 * h, true, w, st, kWideSub,
+                   sub * ld, sub * 2 * h, pstride, beta) ||
+            !rm_tn(h, d, sub, e, h, vb, ld, slot + 2 * hd_elems, d, true, w, st, kWideSub,
+                   sub * h, sub * ld, pstride, beta))
           return ZM_ERR_HIP;
       }
       if (rest > 0) {  // the remainder tokens add into slot 0
         const int64_t r0 = sub * kWideSub;
         const float rb = (sub > 0 || blk > 0) ? 1.f : 0.f;
-        if (!rm_tn(2 * h, d, rest, ab + r0 * 2 * h, 2 * h, kb + r0 * ld, ld, slot, d, true, w, st,
-                   1, 0, 0, 0, rb) ||
-            !rm_tn(d, h, rest, vb + r0 * ld, ld, e + r0 * h, h, slot + 2 * hd_elems, h, true, w,
+        if (!rm_tn(d, 2 * h, rest, kb + r0 * ld, ld, ab + r0 * 2 * h, 2 * h, slot, 2 * h, true, w,
+                   st, 1, 0, 0, 0, rb) ||
+            !rm_tn(h, d, rest, e + r0 * h, h, vb + r0 * ld, ld, slot + 2 * hd_elems, d, true, w,
                    st, 1, 0, 0, 0, rb))
           return ZM_ERR_HIP;
       }

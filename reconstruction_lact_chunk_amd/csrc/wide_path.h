@@ -19,8 +19,10 @@ struct WideBufs {
   void* lt_ws;        // GEMM library workspace
   size_t lt_ws_bytes;
   void* ns;           // Newton-Schulz buffers (with that step rule), else null
+  float* sum;         // the slots' sum [heads][3][h d] in natural layouts (with an update)
   uint16_t* ab;       // token-block buffers: [rows][2 h] then [rows][h], bf16
-  float* part;        // partial sums [kWideSub][heads][3][h d], at the end of the workspace
+  float* part;        // partial sums [kWideSub][heads][3 h d] (transposed; see launch_wide_tsum),
+                      // at the end of the workspace
   bool fits;          // every buffer above lies inside the workspace, block buffers below part
 };
 
@@ -35,13 +37,15 @@ size_t wide_extra_bytes(int heads, int d, int h, int64_t n_kv, int64_t n_q, bool
 WideBufs wide_bufs(void* ws, size_t ws_bytes, size_t base, int heads, int d, int h, int64_t n_kv,
                    int64_t n_q, bool ns);
 
-// Newton-Schulz of every matrix of the summed partials part0 ([heads][3][h d]),
-// in place; ns_ws holds wide_ns_bytes().
+// Newton-Schulz of every matrix of the summed partials part0 ([heads][3][h d],
+// natural layouts), in place; ns_ws holds wide_ns_bytes().
 size_t wide_ns_bytes(int heads, int d, int h);
 int wide_newton_schulz(float* part0, int heads, int d, int h, void* ns_ws, void* lt_ws,
                        size_t lt_bytes, hipStream_t st);
 
-// Minus the chunk gradient over n tokens into w.part (one slot per block).
+// Minus the chunk gradient over n tokens into the kWideSub partial slots of
+// w.part (sub-block i of every block adds into slot i), each slot transposed:
+// per head [D1; D3]^T (d x 2h, row-major), then D2^T (h x d).
 int wide_update(int heads, int d, int h, int64_t ld, int64_t n, const uint16_t* k,
                 const uint16_t* v, const float* eta, const WSet& wb, const WideBufs& w,
                 hipStream_t st);
@@ -64,6 +68,10 @@ hipError_t launch_wide_fwd_gate_update(const uint16_t* k, int64_t ldk, int64_t n
                                        const uint16_t* w1, const uint16_t* w3, int d, int h,
                                        const float* eta, int64_t eta_ld, uint16_t* gab,
                                        int64_t ldab, uint16_t* e, int64_t lde, hipStream_t st);
+// sum = the `splits` transposed slots of part added in slot order, in the
+// natural layouts [heads][3][h d] (W1, W3 as [h][d], W2 as [d][h]).
+hipError_t launch_wide_tsum(const float* part, int splits, int heads, int d, int h, float* sum,
+                            hipStream_t st);
 hipError_t launch_wide_reduce(const float* part, int splits, int heads, int d, int h,
                               const float* w1, const float* w2, const float* w3, float* o1,
                               float* o2, float* o3, int renorm, const WSet* out_bf16,

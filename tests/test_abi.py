@@ -157,11 +157,13 @@ def test_full_width_shape_workspace_and_limits():
     assert base == sets + gemm_ws
     blk = 131072
     # token-block buffers (3 h bf16 per token, at most one block); 8 fp32
-    # partial slots of 3 h d (one for fewer than 8 tokens)
-    assert ws_size(de, 1000, 0)[1] == base + 1000 * 3 * 2048 * 2 + 8 * 3 * welems * 4
-    assert ws_size(de, 5, 0)[1] == base + 5 * 3 * 2048 * 2 + 3 * welems * 4
+    # partial slots of 3 h d (one for fewer than 8 tokens), and with an update
+    # one more 3 h d for the slots' sum in natural layouts
+    slot = 3 * welems * 4
+    assert ws_size(de, 1000, 0)[1] == base + 1000 * 3 * 2048 * 2 + 8 * slot + slot
+    assert ws_size(de, 5, 0)[1] == base + 5 * 3 * 2048 * 2 + slot + slot
     assert ws_size(de, 0, 1000)[1] == base + 1000 * 3 * 2048 * 2
-    assert ws_size(de, 200_000, 10)[1] == base + blk * 3 * 2048 * 2 + 8 * 3 * welems * 4
+    assert ws_size(de, 200_000, 10)[1] == base + blk * 3 * 2048 * 2 + 8 * slot + slot
     assert ws_size(desc(heads=1, d=1024, h=2048, io=zm.F32), 10, 10)[0] == zm.ERR_UNSUPPORTED
     # the Newton-Schulz rule adds its iteration buffers (fp32 X, B X, A, A^2 and
     # the bf16 planes of X and A for the three matrices, plus norm partials)
