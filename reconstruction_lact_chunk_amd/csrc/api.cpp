@@ -34,7 +34,7 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10300;  // 1.3.0
+constexpr int kVersion = 10301;  // 1.3.1
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 

@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10300
+    assert zm.version() == 10301
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
