@@ -191,6 +191,37 @@ def stage_ms(torch, zm, fn, steps=5):
     return out
 
 
+# The plain bf16 GEMM timed beside the headline for context: the layer's input
+# projection (961,800 tokens of width 1024 to 3072 columns), through torch's
+# vendor BLAS.  It shows what the chip's own dense GEMM sustains on the same
+# box in the same process; it is not part of the timed path.
+CONTEXT_GEMM = (961800, 1024, 3072)
+
+
+def plain_gemm_context(dev, torch, reps=5, warmup=2):
+    m, k, n = CONTEXT_GEMM
+    g = torch.Generator(device=dev).manual_seed(12345)
+    a = torch.randn(m, k, device=dev, dtype=torch.bfloat16, generator=g)
+    b = torch.randn(k, n, device=dev, dtype=torch.bfloat16, generator=g).contiguous()
+    for _ in range(warmup):
+        c = torch.matmul(a, b)
+    torch.cuda.synchronize(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        c = torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    tflops = 2.0 * m * k * n / (ms / 1e3) / 1e12
+    return {"what": f"plain bf16 GEMM {m:,} x {k} by {k} x {n} (the layer's input projection), "
+                    "torch.matmul through the vendor BLAS, same process and box as the headline",
+            "ms": round(ms, 4), "achieved_tflops": round(tflops, 1),
+            "frac_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4)}
+
+
 def run_configs(dev, torch, zm, WL, f700_inputs, seed):
     """The other configurations of the benchmark, each timed in its own region
     on the same stream: throughput, fraction of the bf16 matrix peak and, for
@@ -592,6 +623,7 @@ def main():
 
     if wl.name == "f700" and not args.no_configs and rule == zm.STEP_GRADIENT and renorm:
         result["configs"] = run_configs(dev, torch, zm, WL, x, args.seed)
+        result["context"] = {"plain_bf16_gemm": plain_gemm_context(dev, torch)}
 
     if not args.no_cpu_baseline:
         sample = args.cpu_sample_tokens
