@@ -115,7 +115,7 @@ Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
   L.set_b = set_bytes;
   L.part = 2 * set_bytes;
   if (is_wide(d)) {
-    L.plan = UpdatePlan{(int)wide_splits(n_kv), kWideBlock};
+    L.plan = UpdatePlan{(int)wide_splits(n_kv), kWideBlock, 1};
     L.total = L.part + wide_extra_bytes(d->heads, d->d_head, d->d_hidden, n_kv, n_q,
                                         d->step_rule == ZM_STEP_NEWTON_SCHULZ);
     return L;
@@ -124,7 +124,9 @@ Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
   // slots for any update of at most n_kv tokens (see update_slots), then one
   // float per update workgroup for the virtual loss
   const int slots = update_slots(n_kv, d->heads, d->d_hidden);
-  const int nsl = d->d_hidden / kHidPerWg > 0 ? d->d_hidden / kHidPerWg : 1;
+  // the loss's block sums: one per (slot, head, hidden slice), slices of a
+  // two-token-group plan (64 hidden units) included
+  const int nsl = d->d_hidden / (kHidPerWg / 2) > 0 ? d->d_hidden / (kHidPerWg / 2) : 1;
   L.loss = L.part + round_up((size_t)slots * 3 * welems * sizeof(float), 256);
   L.total = L.loss + round_up((size_t)slots * d->heads * nsl * sizeof(float), 256);
   return L;
@@ -272,7 +274,8 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
     }
   }
   if (loss)  // n = 0: zeros
-    ZM_HIP(launch_loss_sum(loss_part, n > 0 ? L.plan.splits : 0, d->heads, d->d_hidden, loss, st));
+    ZM_HIP(launch_loss_sum(loss_part, n > 0 ? L.plan.splits : 0, d->heads,
+                           plan_slices(L.plan, d->d_hidden), loss, st));
   return finish_update(d, n, w1, w2, w3, o1, o2, o3, part, L.plan.splits, emit, st);
 }
 

@@ -15,7 +15,7 @@
 
 namespace zm {
 
-template <int D, int HID>
+template <int D, int HID, int TG>
 __global__ __launch_bounds__(512) void k_frame_bf16(
     const uint16_t* __restrict__ qp, uint16_t* __restrict__ op, int64_t n_q,
     const uint16_t* __restrict__ kp, const uint16_t* __restrict__ vp,
@@ -24,11 +24,11 @@ __global__ __launch_bounds__(512) void k_frame_bf16(
     const uint16_t* __restrict__ w3b, const uint16_t* __restrict__ w2b,
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk_u,
     int upd_blocks, int64_t chunk_a) {
-  constexpr int LU = UpdCfg<D, HID>::LDS_ELEMS, LA = AppCfg<D, HID>::LDS_ELEMS;
+  constexpr int LU = UpdCfg<D, HID, TG>::LDS_ELEMS, LA = AppCfg<D, HID>::LDS_ELEMS;
   __shared__ __attribute__((aligned(16))) uint16_t lds[LU > LA ? LU : LA];
   if ((int)blockIdx.x < upd_blocks)
-    update_tiles<D, HID>(blockIdx.x, lds, kp, vp, eta, n_kv, ld, heads, w1b, w3b, w2tb, part,
-                         splits, chunk_u);
+    update_tiles<D, HID, false, TG>(blockIdx.x, lds, kp, vp, eta, n_kv, ld, heads, w1b, w3b,
+                                    w2tb, part, splits, chunk_u);
   else
     apply_tiles<D, HID>(blockIdx.x - upd_blocks, lds, qp, op, n_q, ld, heads, w1b, w3b, w2b,
                         chunk_a);
@@ -39,7 +39,8 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
                              int heads, int d, int h, WSet w, float* part, UpdatePlan plan,
                              hipStream_t st) {
   if (plan.splits <= 0 || n_kv <= 0 || n_q <= 0) return hipErrorInvalidValue;
-  const int nsl = h / kHidPerWg;
+  if (plan.tg != 1 && plan.tg != 2) return hipErrorInvalidValue;
+  const int nsl = plan_slices(plan, h);
   const int64_t pairs = (int64_t)heads * plan.splits;
   const int upd_blocks = (int)(ceil_div(pairs, 8) * 8 * nsl);
   ApplyPlan ap = plan_apply(n_q, heads, kTargetWgs - upd_blocks);
@@ -48,16 +49,24 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
   // the update's workgroups instead.
   if (ap.chunk > 2 * plan.chunk) ap = plan_apply(n_q, heads);
   const unsigned blocks = (unsigned)(upd_blocks + (int64_t)heads * ap.splits);
-#define ZM_LAUNCH_FRAME(DD, HH)                                                                 \
-  hipLaunchKernelGGL((k_frame_bf16<DD, HH>), dim3(blocks), dim3(512), 0, st, q, o, n_q, k, v,   \
-                     eta, n_kv, ld, heads, w.w1b, w.w3b, w.w2b, w.w2tb, part, plan.splits,       \
+#define ZM_LAUNCH_FRAME_TG(DD, HH, TT)                                                          \
+  hipLaunchKernelGGL((k_frame_bf16<DD, HH, TT>), dim3(blocks), dim3(512), 0, st, q, o, n_q, k,  \
+                     v, eta, n_kv, ld, heads, w.w1b, w.w3b, w.w2b, w.w2tb, part, plan.splits,    \
                      plan.chunk, upd_blocks, ap.chunk)
+#define ZM_LAUNCH_FRAME(DD, HH)          \
+  do {                                   \
+    if (plan.tg == 2)                    \
+      ZM_LAUNCH_FRAME_TG(DD, HH, 2);     \
+    else                                 \
+      ZM_LAUNCH_FRAME_TG(DD, HH, 1);     \
+  } while (0)
   if (d == 128 && h == 256) ZM_LAUNCH_FRAME(128, 256);
   else if (d == 128 && h == 128) ZM_LAUNCH_FRAME(128, 128);
   else if (d == 64 && h == 256) ZM_LAUNCH_FRAME(64, 256);
   else if (d == 64 && h == 128) ZM_LAUNCH_FRAME(64, 128);
   else return hipErrorInvalidValue;
 #undef ZM_LAUNCH_FRAME
+#undef ZM_LAUNCH_FRAME_TG
   return hipGetLastError();
 }
 

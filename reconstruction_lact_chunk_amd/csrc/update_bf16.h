@@ -36,19 +36,35 @@
 
 namespace zm {
 
-template <int D, int HID>
+// TG token groups: with TG = 1 the 8 waves of a workgroup own 8 x 16 hidden
+// units and share every 32-token tile; with TG = 2 they are 4 hidden-unit
+// groups x 2 token groups, a "tile" is 64 tokens (32 per token group) and the
+// workgroup owns 64 hidden units.  TG = 2 writes half the partial sums per
+// workgroup (the two token groups' accumulators are added in the workgroup
+// first), which pays on short chunks such as a streamed frame, where writing
+// and re-reading the partial sums is a large part of the time.
+template <int D, int HID, int TG = 1>
 struct UpdCfg {
-  static constexpr int T = kTok;
-  static constexpr int NSL = HID / kHidPerWg;   // hidden slices (workgroups) per head and chunk
+  static constexpr int T = kTok;                // tokens per token group and tile
+  static constexpr int HPW = 16 * kWaves / TG;  // hidden units per workgroup
+  static constexpr int NSL = HID / HPW;         // hidden slices (workgroups) per head and chunk
   static constexpr int KS = D / 32;             // forward k-steps
   static constexpr int MB = D / 16;             // 16-row blocks along d
   static constexpr int CPT = D / 8;             // 16-byte chunks per token row
-  static constexpr int ITEMS = T * CPT;         // staging items per tile
-  static constexpr int TILE = T * (D + 16);      // elements per padded tile
-  static constexpr int BUF = 2 * TILE;           // elements per LDS buffer (K tile, V_eta tile)
-  static constexpr int NBUF = 8;                 // LDS buffers (tile t in buffer t % NBUF)
+  static constexpr int ITEMS = TG * T * CPT;    // staging items per tile
+  static constexpr int TILE = T * (D + 16);     // elements per padded 32-token tile
+  static constexpr int SUB = 2 * TILE;          // one token group's K and V_eta tiles
+  static constexpr int BUF = TG * SUB;          // elements per LDS buffer
+  static constexpr int NBUF = TG == 1 ? 8 : 4;  // LDS buffers (tile t in buffer t % NBUF)
+  static constexpr int LOOK = TG == 1 ? 3 : 2;  // tile t + LOOK is staged in iteration t
   static constexpr int LDS_ELEMS = NBUF * BUF;
-  static_assert(ITEMS <= kWaves * 64, "one staging item per thread at most");
+  static constexpr int IPT = (ITEMS + kWaves * 64 - 1) / (kWaves * 64);  // staging items per thread
+  static_assert(TG == 1 || TG == 2, "token groups");
+  static_assert(HID % HPW == 0, "hidden slices");
+  static_assert(IPT <= TG, "staging items per thread");
+  // TG = 2 epilogue: one token group's three accumulator sets pass through LDS
+  static_assert(TG == 1 || (kWaves / TG) * 3 * (D / 16) * 64 * 16 <= LDS_ELEMS * 2,
+                "accumulator exchange fits the LDS buffer");
 };
 
 // Tile layout: row r (token) of D bf16, rows padded by 32 bytes.  gfx950 LDS
@@ -107,15 +123,15 @@ __device__ __forceinline__ void gate_backward(float x, float b, float e, float& 
 // slice]: the per-token loss -eta_i f(k_i)^T v_i = -eta_i u_i . W2^T v_i of
 // the review of ZipMap, Method 2, Eq. (2), summed, is ln(2) times the sum of
 // those block values.
-template <int D, int HID, bool LOSS = false>
+template <int D, int HID, bool LOSS = false, int TG = 1>
 __device__ __forceinline__ void update_tiles(
     int blk, uint16_t* __restrict__ lds, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const float* __restrict__ eta, int64_t n, int64_t ld,
     int heads, const uint16_t* __restrict__ w1b, const uint16_t* __restrict__ w3b,
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk,
     float* __restrict__ loss_part = nullptr) {
-  using C = UpdCfg<D, HID>;
-  constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT;
+  using C = UpdCfg<D, HID, TG>;
+  constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT, IPT = C::IPT;
 
   // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
   // over the 8 XCDs; the slices of one (head, chunk) get ids 8 apart, so they
@@ -128,11 +144,13 @@ __device__ __forceinline__ void update_tiles(
   const int head = pair % heads, chunk_id = pair / heads;
   const int64_t t_begin = (int64_t)chunk_id * chunk;
   const int64_t t_end = (t_begin + chunk < n) ? t_begin + chunk : n;
-  const int ntiles = t_end > t_begin ? (int)ceil_div(t_end - t_begin, T) : 0;
+  const int ntiles = t_end > t_begin ? (int)ceil_div(t_end - t_begin, TG * T) : 0;  // tiles of TG * T tokens
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
-  const int j0 = slice * kHidPerWg + w * 16;  // first hidden unit of this wave
+  constexpr int WPG = kWaves / TG;            // waves per token group
+  const int tg = w / WPG;                     // this wave's token group
+  const int j0 = slice * C::HPW + (w % WPG) * 16;  // first hidden unit of this wave
 
   // Forward B operands: lane holds W[j0 + c][32 ks + 8 g .. +7].
   bf16x8 w1f[KS], w3f[KS], w2f[KS];
@@ -155,52 +173,81 @@ __device__ __forceinline__ void update_tiles(
   }
   float lacc = 0.f;   // LOSS: this lane's sum of u' e
 
-  // ---- staging: one 16-byte chunk of k and of v per thread ---------------
-  const bool has_item = tid < C::ITEMS;
-  const int s_tok = tid / CPT, s_ch = tid - (tid / CPT) * CPT;
+  // ---- staging: IPT 16-byte chunks of k and of v per thread -------------
+  // Item i = tid + 512 q of a tile is token row i / CPT (row r of token group
+  // r / 32) and 16-byte chunk i % CPT.
   struct Staged {
-    u32x4 k, v;
-    float e;
+    u32x4 k[IPT], v[IPT];
+    float e[IPT];
   };
-  // Per-lane element offsets of this thread's staging chunk inside a tile;
-  // the tile base is uniform, so loads use a scalar base + vector offset.
-  const int lane_tok_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
-  const int lane_eta_off = (has_item ? s_tok : 0) * heads + head;
+  bool has_item[IPT];
+  int s_tok[IPT], s_ch[IPT], lane_tok_off[IPT], lane_eta_off[IPT];
+#pragma unroll
+  for (int q = 0; q < IPT; ++q) {
+    const int it_ = tid + q * kWaves * 64;
+    has_item[q] = it_ < C::ITEMS;
+    s_tok[q] = it_ / CPT;
+    s_ch[q] = it_ - (it_ / CPT) * CPT;
+    // Per-lane element offsets of this thread's staging chunk inside a tile;
+    // the tile base is uniform, so loads use a scalar base + vector offset.
+    lane_tok_off[q] = has_item[q] ? s_tok[q] * (int)ld + head * D + 8 * s_ch[q] : head * D;
+    lane_eta_off[q] = (has_item[q] ? s_tok[q] : 0) * heads + head;
+  }
+  constexpr int TT = TG * T;  // tokens per tile
+  constexpr int QROWS = kWaves * 64 / CPT;  // token rows between a thread's staging items
+  static_assert(IPT == 1 || C::ITEMS % (kWaves * 64) == 0, "every thread has all its items");
   auto fetch = [&](int it) {
-    const int64_t t0 = t_begin + (int64_t)it * T;
+    const int64_t t0 = t_begin + (int64_t)it * TT;
     Staged r;
-    if (t0 + T <= t_end) {  // whole tile in range (uniform branch)
-      r.k = *(const u32x4*)(kp + t0 * ld + lane_tok_off);
-      r.v = *(const u32x4*)(vp + t0 * ld + lane_tok_off);
-      r.e = eta[t0 * heads + lane_eta_off];
+    if (t0 + TT <= t_end) {  // whole tile in range (uniform branch)
+      // item q is item 0 moved by q * QROWS token rows: one per-lane offset,
+      // the rest in the uniform base
+#pragma unroll
+      for (int q = 0; q < IPT; ++q) {
+        const int64_t tq = t0 + (int64_t)q * QROWS;
+        r.k[q] = *(const u32x4*)(kp + tq * ld + lane_tok_off[0]);
+        r.v[q] = *(const u32x4*)(vp + tq * ld + lane_tok_off[0]);
+        r.e[q] = eta[tq * heads + lane_eta_off[0]];
+      }
     } else {
       // Tail tile: out-of-range tokens get eta = 0 and a real token's k and v
       // (finite values; eta = 0 zeroes their contribution, since e, ga, gb
       // and V_eta all carry eta).
       // Tiles past the last one (prefetch overrun) read the chunk's first
       // token, so every load stays inside the token array.
-      const bool ok = has_item && t0 + s_tok < t_end;
-      const int64_t tc = ok ? t0 + s_tok : (t0 < t_end ? t0 : t_begin);
-      const int col = has_item ? 8 * s_ch : 0;
-      r.k = *(const u32x4*)(kp + tc * ld + head * D + col);
-      r.v = *(const u32x4*)(vp + tc * ld + head * D + col);
-      const float e0 = eta[tc * heads + head];
-      r.e = ok ? e0 : 0.f;
+#pragma unroll
+      for (int q = 0; q < IPT; ++q) {
+        const bool ok = has_item[q] && t0 + s_tok[q] < t_end;
+        const int64_t tc = ok ? t0 + s_tok[q] : (t0 < t_end ? t0 : t_begin);
+        const int col = has_item[q] ? 8 * s_ch[q] : 0;
+        r.k[q] = *(const u32x4*)(kp + tc * ld + head * D + col);
+        r.v[q] = *(const u32x4*)(vp + tc * ld + head * D + col);
+        const float e0 = eta[tc * heads + head];
+        r.e[q] = ok ? e0 : 0.f;
+      }
     }
     return r;
   };
   auto stage = [&](int buf, const Staged& r) {
-    if constexpr (C::ITEMS < kWaves * 64) {
-      if (!has_item) return;
-    }
-    uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
-    uint16_t* vtm = ktm + C::TILE;
-    u32x4 vs;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) vs[q] = pack_bf16x2(bf16lo(r.v[q]) * r.e, bf16hi(r.v[q]) * r.e);
-    const int off = tile_off<D>(s_tok, 8 * s_ch);
-    *(u32x4*)(ktm + off) = r.k;
-    *(u32x4*)(vtm + off) = vs;
+    for (int q = 0; q < IPT; ++q) {
+      if (C::ITEMS < (q + 1) * kWaves * 64 && !has_item[q]) continue;  // folds per q
+      // token row s_tok lies in token group s_tok / T
+      const int grp = TG == 1 ? 0 : s_tok[q] / T;
+      uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF + grp * C::SUB;
+      uint16_t* vtm = ktm + C::TILE;
+      u32x4 vs;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        vs[i] = pack_bf16x2(bf16lo(r.v[q][i]) * r.e[q], bf16hi(r.v[q][i]) * r.e[q]);
+      const int off = tile_off<D>(TG == 1 ? s_tok[q] : s_tok[q] % T, 8 * s_ch[q]);
+      *(u32x4*)(ktm + off) = r.k[q];
+      *(u32x4*)(vtm + off) = vs;
+    }
+  };
+  // this wave's K tile in buffer buf (its V_eta tile follows at + TILE)
+  auto tile_base = [&](int buf) -> uint16_t* {
+    return lds + (buf & (C::NBUF - 1)) * C::BUF + (TG == 1 ? 0 : tg * C::SUB);
   };
 
   // Transposing-read addresses: lane (g, s) loads 4 columns 16 m + 4 (s % 4)
@@ -216,7 +263,7 @@ __device__ __forceinline__ void update_tiles(
 
   // forward A = K W1^T, B = K W3^T, E = V_eta W2 on one tile (24 MFMAs)
   auto forward = [&](int buf) {
-    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
+    const uint16_t* ktm = tile_base(buf);
     const uint16_t* vtm = ktm + C::TILE;
     Fwd f;
 #pragma unroll
@@ -264,7 +311,7 @@ __device__ __forceinline__ void update_tiles(
 
   // backward D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta (24 MFMAs)
   auto backward = [&](int buf, const Grad& gr) {
-    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
+    const uint16_t* ktm = tile_base(buf);
     const uint16_t* vtm = ktm + C::TILE;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
@@ -287,13 +334,13 @@ __device__ __forceinline__ void update_tiles(
     bf16x8 x, y;
   };
   auto fwd_frag = [&](int buf, int mb, int ks) {  // K and V_eta rows (A operands)
-    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
+    const uint16_t* ktm = tile_base(buf);
     const int off = tile_off<D>(tau(c >> 2, 4 * mb + (c & 3)), 32 * ks + 8 * g);
     return Frag2{as_bf16x8(*(const u32x4*)(ktm + off)),
                  as_bf16x8(*(const u32x4*)(ktm + C::TILE + off))};
   };
   auto bwd_frag = [&](int buf, int m) {  // K^T and V_eta^T column pieces
-    const uint16_t* ktm = lds + (buf & (C::NBUF - 1)) * C::BUF;
+    const uint16_t* ktm = tile_base(buf);
     const int col = 16 * m + 4 * (c & 3);
     const int oa = tile_off<D>(row_a, col), ob = tile_off<D>(row_b, col);
     return Frag2{__builtin_shufflevector(lds_read_tr(ktm + oa), lds_read_tr(ktm + ob),
@@ -323,7 +370,7 @@ __device__ __forceinline__ void update_tiles(
   constexpr int NMICRO = 4 * 13;
   auto step = [&](int t, const Fwd& f, const Grad& prev, Fwd& fn, Grad& cur, bool barrier)
       __attribute__((always_inline)) {
-    const Staged nx = fetch(t + 3);
+    const Staged nx = fetch(t + C::LOOK);
     Frag2 fr[NSLOT];
 #pragma unroll
     for (int j = 0; j < LA; ++j) fr[j] = load_slot(t, j);
@@ -424,34 +471,52 @@ __device__ __forceinline__ void update_tiles(
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int i = 3 * NSLOT; i < NMICRO; ++i) micro(i);
-    stage(t + 3, nx);
+    stage(t + C::LOOK, nx);
     if (barrier) __syncthreads();
     cur = Grad{as_bf16x8(gap), as_bf16x8(gbp), as_bf16x8(up)};
   };
 
-  // Tile t is staged in iteration t - 3 (the prologue stages tiles 0..3),
-  // read by the forward in iteration t - 1 and by the backward in iteration
-  // t + 1.  A barrier closes every even iteration only: a staged tile is
-  // first read two iterations later, and a buffer is rewritten (NBUF = 8)
-  // four iterations after its last read, so a barrier always lies between.
-  // The prologue's four tiles are fetched together, so that their memory
-  // round trips overlap (on a short chunk the prologue is a large part of
-  // the block's time).
+  // TG = 1: tile t is staged in iteration t - 3 (the prologue stages tiles
+  // 0..3), read by the forward in iteration t - 1 and by the backward in
+  // iteration t + 1.  A barrier closes every even iteration only: a staged
+  // tile is first read two iterations later, and a buffer is rewritten
+  // (NBUF = 8) four iterations after its last read, so a barrier always lies
+  // between.  The prologue's four tiles are fetched together, so that their
+  // memory round trips overlap (on a short chunk the prologue is a large part
+  // of the block's time).
+  // TG = 2 (tiles twice as large, NBUF = 4): tile t is staged in iteration
+  // t - 2 and a barrier closes every iteration; a buffer is rewritten two
+  // iterations after its last read.
   if (ntiles > 0) {
-    const Staged s0 = fetch(0), s1 = fetch(1), s2 = fetch(2), s3 = fetch(3);
-    stage(0, s0);
-    stage(1, s1);
-    stage(2, s2);
-    __syncthreads();
-    Fwd fa = forward(0), fb;
-    Grad ga_ = pointwise(fa), gb_;
-    // t = 0: no backward yet
-    if (ntiles > 1) fa = forward(1);
-    stage(3, s3);
-    __syncthreads();
+    Fwd fa, fb;
+    Grad ga_, gb_;
+    if constexpr (TG == 1) {
+      const Staged s0 = fetch(0), s1 = fetch(1), s2 = fetch(2), s3 = fetch(3);
+      stage(0, s0);
+      stage(1, s1);
+      stage(2, s2);
+      __syncthreads();
+      fa = forward(0);
+      ga_ = pointwise(fa);
+      // t = 0: no backward yet
+      if (ntiles > 1) fa = forward(1);
+      stage(3, s3);
+      __syncthreads();
+    } else {
+      const Staged s0 = fetch(0), s1 = fetch(1);
+      stage(0, s0);
+      stage(1, s1);
+      const Staged s2 = fetch(2);
+      __syncthreads();
+      fa = forward(0);
+      ga_ = pointwise(fa);
+      if (ntiles > 1) fa = forward(1);
+      stage(2, s2);
+      __syncthreads();
+    }
     int t = 1;
     for (; t + 2 < ntiles; t += 2) {  // steady state, two iterations per trip
-      step(t, fa, ga_, fb, gb_, false);
+      step(t, fa, ga_, fb, gb_, TG == 2);
       step(t + 1, fb, gb_, fa, ga_, true);
     }
     if (t + 1 < ntiles) {  // one steady iteration left
@@ -482,6 +547,49 @@ __device__ __forceinline__ void update_tiles(
       loss_part[((int64_t)chunk_id * heads + head) * C::NSL + slice] = sum;
     }
   }
+  // TG = 2: the two token groups' accumulators are added (group 0 + group 1:
+  // one fixed order), each group combining and writing half of the 16-row
+  // blocks m of all three sums (group 0 the first half).
+  constexpr int MH = TG == 2 ? MB / 2 : MB;
+  if constexpr (TG == 2) {
+    static_assert(MB % 2 == 0, "blocks split between the token groups");
+    __syncthreads();   // the tile ring (and the loss scratch) is no longer read
+    f32x4* xch = reinterpret_cast<f32x4*>(lds);
+    const int hg = w % WPG;
+    // slot of (hidden group, receiving token group, sum, block m' < MH, lane)
+    auto slot = [&](int to, int mat, int mm) { return (((hg * 2 + to) * 3 + mat) * MH + mm) * 64 + l; };
+    if (tg == 0) {   // hands over blocks MH.., keeps 0..MH-1
+#pragma unroll
+      for (int mm = 0; mm < MH; ++mm) {
+        xch[slot(1, 0, mm)] = acc1[MH + mm];
+        xch[slot(1, 1, mm)] = acc3[MH + mm];
+        xch[slot(1, 2, mm)] = acc2[MH + mm];
+      }
+    } else {         // hands over blocks 0..MH-1, keeps MH..
+#pragma unroll
+      for (int mm = 0; mm < MH; ++mm) {
+        xch[slot(0, 0, mm)] = acc1[mm];
+        xch[slot(0, 1, mm)] = acc3[mm];
+        xch[slot(0, 2, mm)] = acc2[mm];
+      }
+    }
+    __syncthreads();
+    if (tg == 0) {
+#pragma unroll
+      for (int mm = 0; mm < MH; ++mm) {
+        acc1[mm] = acc1[mm] + xch[slot(0, 0, mm)];
+        acc3[mm] = acc3[mm] + xch[slot(0, 1, mm)];
+        acc2[mm] = acc2[mm] + xch[slot(0, 2, mm)];
+      }
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < MH; ++mm) {
+        acc1[MH + mm] = xch[slot(1, 0, mm)] + acc1[MH + mm];
+        acc3[MH + mm] = xch[slot(1, 1, mm)] + acc3[MH + mm];
+        acc2[MH + mm] = xch[slot(1, 2, mm)] + acc2[MH + mm];
+      }
+    }
+  }
   // all three partial sums were accumulated from ga', gb', u', which carry -log2(e)
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -495,6 +603,7 @@ __device__ __forceinline__ void update_tiles(
   float* P = part + ((int64_t)chunk_id * heads + head) * 3 * hd_elems;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
+    if (TG == 2 && (m < MH) != (tg == 0)) continue;   // the other token group writes it
     // acc1/acc3 lane values: D1[j0 + c][16 m + 4 g + i], i = 0..3
     *(f32x4*)(P + (int64_t)(j0 + c) * D + 16 * m + 4 * g) = acc1[m];
     *(f32x4*)(P + hd_elems + (int64_t)(j0 + c) * D + 16 * m + 4 * g) = acc3[m];

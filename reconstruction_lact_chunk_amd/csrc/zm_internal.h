@@ -118,21 +118,40 @@ void set_last_error(const char* fmt, ...);
 // ---- split plan ------------------------------------------------------------
 struct UpdatePlan {
   int splits;        // S: token chunks (partial sums) per head
-  int64_t chunk;     // tokens per chunk, a multiple of kTok
+  int64_t chunk;     // tokens per chunk, a multiple of tg * kTok
+  int tg = 1;        // token groups per workgroup of the bf16 update (1 or 2)
 };
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // The split is a pure function of (n, heads, d_hidden): results never depend
-// on the device or on occupancy.
+// on the device or on occupancy.  Workgroups of 128 hidden units (tg = 1)
+// get chunks of at least kMinTilesPerChunk 32-token tiles, as many chunks as
+// fill the GPU.  When even that leaves compute units idle (a short chunk such
+// as a streamed frame), workgroups of 64 hidden units and two token groups
+// (tg = 2, 64-token tiles) take the same per-wave work with half the partial
+// sums per workgroup.  Hidden widths below 128 keep tg = 1.
 inline UpdatePlan plan_update(int64_t n, int heads, int d_hidden) {
-  UpdatePlan p{0, 0};
+  UpdatePlan p{0, 0, 1};
   if (n <= 0) return p;
   const int nsl = d_hidden / kHidPerWg > 0 ? d_hidden / kHidPerWg : 1;
   int64_t target = kTargetWgs / (int64_t)(heads * nsl);
   if (target < 1) target = 1;
   const int64_t tiles = ceil_div(n, kTok);
   int64_t s = ceil_div(tiles, kMinTilesPerChunk);
+  if (s < target && d_hidden >= kHidPerWg) {
+    // two token groups: 2 nsl slices per head, 64-token tiles
+    int64_t target2 = target / 2;
+    if (target2 < 1) target2 = 1;
+    const int64_t tiles2 = ceil_div(n, 2 * kTok);
+    int64_t s2 = ceil_div(tiles2, kMinTilesPerChunk);
+    if (s2 > target2) s2 = target2;
+    if (s2 < 1) s2 = 1;
+    p.tg = 2;
+    p.chunk = ceil_div(tiles2, s2) * 2 * kTok;
+    p.splits = (int)ceil_div(n, p.chunk);
+    return p;
+  }
   if (s > target) s = target;
   if (s < 1) s = 1;
   p.chunk = ceil_div(tiles, s) * kTok;
@@ -140,11 +159,19 @@ inline UpdatePlan plan_update(int64_t n, int heads, int d_hidden) {
   return p;
 }
 
+// Hidden slices (update workgroups per head and chunk) of a plan.
+inline int plan_slices(const UpdatePlan& p, int d_hidden) {
+  const int hpw = kHidPerWg / p.tg;
+  return d_hidden / hpw > 0 ? d_hidden / hpw : 1;
+}
+
 // Partial-sum slots a workspace reserves for an update over n tokens: the
-// planned split count before rounding.  It never decreases with n and bounds
-// the realized count plan_update(n').splits of every n' <= n (that count is
-// ceil(n' / chunk') with chunk' >= n' / s', so at most s' <= s), which is what
-// lets one workspace, sized for the longest chunk, serve every shorter chunk.
+// planned split count of the tg = 1 plan before rounding.  It never decreases
+// with n and bounds the realized count plan_update(n').splits of every
+// n' <= n (that count is ceil(n' / chunk') with chunk' >= n' / s', so at most
+// s', and a tg = 2 plan's s' is at most the tg = 1 count of the same n'),
+// which is what lets one workspace, sized for the longest chunk, serve every
+// shorter chunk.
 // The realized count alone is not monotonic: 1058 tokens over 16 heads of
 // hidden 256 realize 7 splits, 949 tokens 8.
 inline int update_slots(int64_t n, int heads, int d_hidden) {
@@ -185,13 +212,13 @@ hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int he
                        WSet out, hipStream_t st);
 
 // loss_part non-null: also the virtual loss's per-workgroup sums (splits x
-// heads x h / kHidPerWg floats) for launch_loss_sum.
+// heads x plan_slices floats) for launch_loss_sum.
 hipError_t launch_update_bf16(const uint16_t* k, const uint16_t* v, const float* eta, int64_t n,
                               int64_t ld, int heads, int d, int h, WSet w, float* part,
                               UpdatePlan plan, hipStream_t st, float* loss_part = nullptr);
 // loss[head] from the per-workgroup sums of launch_update_bf16 (splits may be
-// 0: zeros).
-hipError_t launch_loss_sum(const float* loss_part, int splits, int heads, int h, float* loss,
+// 0: zeros); nsl = plan_slices of the update's plan.
+hipError_t launch_loss_sum(const float* loss_part, int splits, int heads, int nsl, float* loss,
                            hipStream_t st);
 
 hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,

@@ -68,10 +68,10 @@ def test_workspace_size_structure():
     st, big = ws_size(de, 961_800, 961_800)
     assert st == 0
     # the partial-sum slots (3 h d fp32 per head each), then one fp32 per
-    # update workgroup (heads x h / 128 per slot) for the virtual loss,
-    # rounded up to 256 bytes
+    # update workgroup for the virtual loss (heads x h / 64 per slot: the
+    # slices of a two-token-group plan), rounded up to 256 bytes
     parts = (big - base) // (3 * welems * 4)
-    assert big == base + parts * 3 * welems * 4 + (parts * 8 * 2 * 4 + 255) // 256 * 256
+    assert big == base + parts * 3 * welems * 4 + (parts * 8 * 4 * 4 + 255) // 256 * 256
     assert 1 <= parts <= 256
     # more tokens never need fewer partial sums; queries need no workspace
     sizes = [ws_size(de, n, 0)[1] for n in (1, 31, 32, 33, 1000, 10_992, 137_400, 961_800)]

@@ -25,15 +25,30 @@ def ceil_div(a, b):
     return (a + b - 1) // b
 
 
-def plan_update(n, heads, d_hidden):
+def plan_update_tg(n, heads, d_hidden):
+    """(splits, chunk, tg): workgroups of 128 hidden units and 32-token tiles
+    (tg = 1), or, when chunks of MIN_TILES tiles would not fill the GPU, of
+    64 hidden units and two token groups over 64-token tiles (tg = 2)."""
     if n <= 0:
-        return 0, 0
+        return 0, 0, 1
     nsl = max(d_hidden // 128, 1)
     target = max(TARGET_WGS // (heads * nsl), 1)
     tiles = ceil_div(n, TOK)
-    s = min(max(ceil_div(tiles, MIN_TILES), 1), target)
+    s = ceil_div(tiles, MIN_TILES)
+    if s < target and d_hidden >= 128:
+        target2 = max(target // 2, 1)
+        tiles2 = ceil_div(n, 2 * TOK)
+        s2 = min(max(ceil_div(tiles2, MIN_TILES), 1), target2)
+        chunk = ceil_div(tiles2, s2) * 2 * TOK
+        return ceil_div(n, chunk), chunk, 2
+    s = min(max(s, 1), target)
     chunk = ceil_div(tiles, s) * TOK
-    return ceil_div(n, chunk), chunk
+    return ceil_div(n, chunk), chunk, 1
+
+
+def plan_update(n, heads, d_hidden):
+    splits, chunk, _ = plan_update_tg(n, heads, d_hidden)
+    return splits, chunk
 
 
 def update_slots(n, heads, d_hidden):
@@ -55,12 +70,12 @@ def plan_apply(n, heads):
     return ceil_div(n, chunk), chunk
 
 
-def fetch_rows_update(t_begin, t_end, it):
-    """Token rows loaded by the 32 staging rows of tile `it`."""
-    t0 = t_begin + it * TOK
+def fetch_rows_update(t_begin, t_end, it, tile=TOK):
+    """Token rows loaded by the staging rows of tile `it` (tile tokens)."""
+    t0 = t_begin + it * tile
     rows = []
-    for s_tok in range(TOK):
-        if t0 + TOK <= t_end:
+    for s_tok in range(tile):
+        if t0 + tile <= t_end:
             rows.append(t0 + s_tok)
         else:
             ok = t0 + s_tok < t_end
@@ -87,18 +102,20 @@ SIZES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 1000, 1374, 10_992, 137_40
 @pytest.mark.parametrize("n", SIZES)
 @pytest.mark.parametrize("heads,d_hidden", [(8, 256), (1, 128), (3, 128), (64, 256)])
 def test_update_chunks_partition_and_loads_in_bounds(n, heads, d_hidden):
-    splits, chunk = plan_update(n, heads, d_hidden)
-    assert chunk % TOK == 0 and splits >= 1
+    splits, chunk, tg = plan_update_tg(n, heads, d_hidden)
+    tile = tg * TOK
+    assert chunk % tile == 0 and splits >= 1
     covered = []
     for c in range(splits):
         tb, te = c * chunk, min(n, c * chunk + chunk)
         assert tb < te, "no empty chunk"
         covered.append((tb, te))
-        ntiles = ceil_div(te - tb, TOK)
-        # the pipeline fetches tiles 0 .. max(3, ntiles + 1): the prologue
-        # fetches tiles 0..3, iteration t fetches tile t + 3
-        for it in range(max(4, ntiles + 2)):
-            for r in fetch_rows_update(tb, te, it):
+        ntiles = ceil_div(te - tb, tile)
+        # tg = 1: the prologue fetches tiles 0..3 and iteration t tile t + 3;
+        # tg = 2: the prologue fetches tiles 0..2 and iteration t tile t + 2
+        look = 3 if tg == 1 else 2
+        for it in range(max(look + 1, ntiles + look - 1)):
+            for r in fetch_rows_update(tb, te, it, tile):
                 assert tb <= r < te <= n
     assert covered[0][0] == 0 and covered[-1][1] == n
     assert all(a[1] == b[0] for a, b in zip(covered, covered[1:]))
@@ -163,6 +180,20 @@ def update_schedule(ntiles):
     return ivs
 
 
+def update_schedule_tg2(ntiles):
+    """Barrier intervals of the two-token-group update (tiles of 64 tokens,
+    4 buffers): tiles 0, 1 staged, barrier; forward(0), forward(1) and
+    staging of tile 2, barrier; then iteration t reads tiles t - 1
+    (backward) and t + 1 (forward) and stages tile t + 2, with a barrier
+    after every iteration; the epilogue reads the last two tiles."""
+    ivs = [{"read": [], "write": [0, 1]},
+           {"read": [0, 1] if ntiles > 1 else [0], "write": [2]}]
+    for t in range(1, ntiles - 1):
+        ivs.append({"read": [t - 1, t + 1], "write": [t + 2]})
+    ivs.append({"read": [ntiles - 2, ntiles - 1] if ntiles > 1 else [0], "write": []})
+    return ivs
+
+
 def apply_q_schedule(ntiles):
     ivs = [{"read": [], "write": [0, 1]},                        # prologue staging
            {"read": [0], "write": []},                           # phase1(0); barrier
@@ -201,6 +232,7 @@ def apply_o_schedule(ntiles):
 def test_pipeline_buffer_schedules_are_hazard_free(ntiles):
     # tiles past the last are staged (prefetch overrun) but never read
     check_schedule(update_schedule(ntiles), 8)
+    check_schedule(update_schedule_tg2(ntiles), 4)
     check_schedule(apply_q_schedule(ntiles), 2)
     check_schedule(apply_u_schedule(ntiles), 2)
     sched = apply_o_schedule(ntiles)
@@ -218,6 +250,25 @@ def test_update_schedule_needs_eight_buffers_or_six():
     with pytest.raises(AssertionError):
         for ntiles in range(6, 14):
             check_schedule(update_schedule(ntiles), 5)
+
+
+def test_two_token_group_schedule_needs_four_buffers():
+    for ntiles in range(4, 14):
+        check_schedule(update_schedule_tg2(ntiles), 4)
+    with pytest.raises(AssertionError):
+        for ntiles in range(4, 14):
+            check_schedule(update_schedule_tg2(ntiles), 3)
+
+
+def test_short_chunks_take_two_token_groups():
+    # a streamed 1374-token frame, 8 heads of hidden 256: 6 chunks of 256
+    # tokens in workgroups of 64 hidden units (192 workgroups)
+    assert plan_update_tg(1374, 8, 256) == (6, 256, 2)
+    # a chunk long enough to fill the GPU with 4-tile chunks keeps tg = 1
+    assert plan_update_tg(2048, 8, 256)[2] == 1
+    assert plan_update_tg(961_800, 8, 256)[2] == 1
+    # hidden 128 has one 128-unit slice per head: tg = 2 gives two
+    assert plan_update_tg(1000, 3, 128)[2] == 2
 
 
 def test_schedule_checker_catches_a_missing_barrier():
