@@ -18,7 +18,11 @@
 //   forward   A = K W1^T, B = K W3^T, E = V_eta W2   (M = tokens, K = d)
 //   pointwise SiLU / gate backward in registers
 //   backward  D1^T += K^T Ga, D3^T += K^T Gb, D2^T += U^T V_eta  (K = tokens)
-// software-pipelined over tiles (see the main loop).
+// software-pipelined over tiles (see the main loop).  For short chunks the
+// planner picks a second shape (TG = 2, UpdCfg): 64 hidden units per
+// workgroup, its waves 4 hidden-unit groups x 2 token groups over 64-token
+// tiles, whose accumulators are added in the workgroup before the partial
+// sums are written (half the partial sums per workgroup).
 // The backward contracts over tokens, so its K / V_eta operands are read
 // from the token-major LDS tile with the gfx950 transposing LDS load
 // (ds_read_b64_tr_b16): within each 16-lane group, lane i receives element
