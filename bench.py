@@ -581,7 +581,7 @@ def main():
                      if dom == "update" else
                      "apply stage (k_wide_rows read + hipBLASLt output GEMM)")
         else:
-            kname = "k_update_bf16<128,256>" if dom == "update" else "k_apply_bf16<128,256>"
+            kname = "k_update_bf16<128,256,1>" if dom == "update" else "k_apply_bf16<128,256>"
         result["roofline"] = {
             "kernel": kname,
             "bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,

@@ -213,6 +213,14 @@ __device__ __forceinline__ void update_tiles(
         r.v[q] = *(const u32x4*)(vp + tq * ld + lane_tok_off[0]);
         r.e[q] = eta[tq * heads + lane_eta_off[0]];
       }
+    } else if (TG == 2 && t0 >= t_end) {
+      // a tile past the last one (prefetch overrun): staged, never read
+#pragma unroll
+      for (int q = 0; q < IPT; ++q) {
+        r.k[q] = u32x4{0u, 0u, 0u, 0u};
+        r.v[q] = r.k[q];
+        r.e[q] = 0.f;
+      }
     } else {
       // Tail tile: out-of-range tokens get eta = 0 and a real token's k and v
       // (finite values; eta = 0 zeroes their contribution, since e, ga, gb
