@@ -18,7 +18,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 // ---- tiling constants shared by planner and kernels -----------------------
 constexpr int kTok = 32;          // tokens per LDS tile (bf16 kernels); chunks are multiples
 constexpr int kWaves = 8;         // waves per workgroup of the bf16 kernels
-constexpr int kHidPerWg = 128;    // hidden units owned by one bf16 update workgroup
+constexpr int kHidPerWg = 128;    // hidden units of a bf16 update workgroup (half with two token groups)
 constexpr int kHidPerWgF32 = 64;  // hidden units owned by one fp32 update workgroup
 constexpr int kTargetWgs = 256;   // MI355X compute units: one workgroup each
 constexpr int kMinTilesPerChunk = 4;
