@@ -34,7 +34,7 @@ using namespace zm;
 
 namespace {
 
-constexpr int kVersion = 10301;  // 1.3.1
+constexpr int kVersion = 10400;  // 1.4.0
 constexpr int64_t kMaxChunks = (int64_t)1 << 24;
 constexpr int kMaxInnerSteps = 64;
 
@@ -101,25 +101,28 @@ struct Ws {
 };
 
 struct Layout {
-  size_t set_a, set_b, part, loss, total;   // loss: virtual-loss block sums (narrow heads)
+  size_t set_a, set_b, sync, part, loss, total;   // loss: virtual-loss block sums (narrow heads)
   UpdatePlan plan;
 };
 
-// Workspace: two bf16 weight sets (4 arrays each), then the partial sums (or,
-// for the full width, the token-block buffers and the partial sums).
+// Workspace: two bf16 weight sets (4 arrays each), then for the narrow heads
+// the shared launch's sync words (frame_sync_words) and the partial sums (for
+// the full width: the token-block buffers and the partial sums).  Offsets up
+// to the partial sums do not depend on the token counts.
 Layout layout(const zm_ttt_desc* d, int64_t n_kv, int64_t n_q) {
   Layout L{};
   const size_t welems = (size_t)d->heads * d->d_hidden * d->d_head;
   const size_t set_bytes = round_up(4 * welems * sizeof(uint16_t), 256);
   L.set_a = 0;
   L.set_b = set_bytes;
-  L.part = 2 * set_bytes;
+  L.sync = L.part = 2 * set_bytes;
   if (is_wide(d)) {
     L.plan = UpdatePlan{(int)wide_splits(n_kv), kWideBlock, 1};
     L.total = L.part + wide_extra_bytes(d->heads, d->d_head, d->d_hidden, n_kv, n_q,
                                         d->step_rule == ZM_STEP_NEWTON_SCHULZ);
     return L;
   }
+  L.part = L.sync + round_up(frame_sync_words(d->heads) * sizeof(unsigned), 256);
   L.plan = plan_update(n_kv, d->heads, d->d_hidden);
   // slots for any update of at most n_kv tokens (see update_slots), then one
   // float per update workgroup for the virtual loss
@@ -340,28 +343,36 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
   reuse = reuse && bf16;
   emit = emit && bf16;
   const int updates = do_update ? inner : 0;
+  unsigned* const sync = is_wide(d) ? nullptr : (unsigned*)((char*)ws.p + L.sync);
   if (order == ZM_APPLY_THEN_UPDATE || updates == 0) {
     // Read the chunk with the incoming W; the first update shares that cast.
     if (bf16 && !reuse) {
       Scoped s(kStageCast, st);
-      ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
+      ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st, sync,
+                         sync ? (int)frame_sync_words(d->heads) : 0));
     }
     int first = 0;
     if (bf16 && !is_wide(d) && updates > 0 && n > 0) {
       // The read and the first update's partial sums use only the incoming W:
-      // one launch for both (both stages' profile events bracket it).
+      // one launch for both (both stages' profile events bracket it), which
+      // for short frames also reduces them.
       float* part = (float*)((char*)ws.p + L.part);
       ZM_TRY(check_part_range(L.part, L.plan.splits, welems, ws.bytes));
+      const WSet* out = (emit && updates == 1) ? &a : nullptr;
+      const bool fuse = d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, n);
+      const FrameReduce fr{sync, ReduceOut{w1, w2, w3, w1, w2, w3,
+                                           out ? *out : WSet{nullptr, nullptr, nullptr, nullptr},
+                                           d->renorm, out ? 1 : 0}};
       {
         Scoped su(kStageUpdate, st);
         Scoped sa(kStageApply, st);
         ZM_HIP(launch_frame_bf16((const uint16_t*)q, (uint16_t*)o, n, (const uint16_t*)k,
                                  (const uint16_t*)v, eta, n, d->ld_tok, d->heads, d->d_head,
-                                 d->d_hidden, a, part, L.plan, st));
+                                 d->d_hidden, a, part, L.plan, st, fuse ? &fr : nullptr));
       }
       // the frame kernel has read set a before the reduce rewrites it
-      ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits,
-                           (emit && updates == 1) ? &a : nullptr, st));
+      if (!fuse)
+        ZM_TRY(finish_update(d, n, w1, w2, w3, w1, w2, w3, part, L.plan.splits, out, st));
       first = 1;
     } else {
       ZM_TRY(run_apply(d, n, q, o, w1, w2, w3, a, ws, st));
@@ -398,6 +409,7 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
   const Layout L0 = layout(d, 0, 0);  // set and partial-sum offsets do not depend on n
   const WSet a = carve_set(ws.p, L0.set_a, (size_t)d->heads * d->d_hidden * d->d_head);
   float* part = (float*)((char*)ws.p + L0.part);
+  unsigned* const sync = (unsigned*)((char*)ws.p + L0.sync);
   const size_t row = (size_t)d->ld_tok * sizeof(uint16_t);
   const int hd = d->heads, dh = d->d_head, hh = d->d_hidden;
   auto tok = [&](const char* base, int64_t c) { return (const uint16_t*)(base + offsets[c] * row); };
@@ -413,17 +425,22 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
     const UpdatePlan plan = plan_update(len(c), hd, hh);
     ZM_TRY(check_part_range(L0.part, plan.splits, (size_t)hd * hh * dh, ws.bytes));
     const float* e = eta + offsets[c] * hd;
+    const bool fuse = rc >= 0 && d->step_rule == ZM_STEP_GRADIENT &&
+                      frame_fuses_reduce(hd, len(c));
     {
       Scoped su(kStageUpdate, st);
       if (rc >= 0) {
         Scoped sa(kStageApply, st);
+        const FrameReduce fr{sync, ReduceOut{w1, w2, w3, w1, w2, w3, a, d->renorm, 1}};
         ZM_HIP(launch_frame_bf16(tok(q, rc), (uint16_t*)(o + offsets[rc] * row), len(rc), tok(k, c),
-                                 tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part, plan, st));
+                                 tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part, plan, st,
+                                 fuse ? &fr : nullptr));
       } else {
         ZM_HIP(launch_update_bf16(tok(k, c), tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part,
                                   plan, st));
       }
     }
+    if (fuse) return ZM_OK;
     return finish_update(d, len(c), w1, w2, w3, w1, w2, w3, part, plan.splits, &a, st);
   };
   bool cast = false;
@@ -433,7 +450,7 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
     const bool upd = update_mask == nullptr || update_mask[c] != 0;
     if (!cast) {
       Scoped s(kStageCast, st);
-      ZM_HIP(launch_cast(w1, w2, w3, hd, dh, hh, a, st));
+      ZM_HIP(launch_cast(w1, w2, w3, hd, dh, hh, a, st, sync, (int)frame_sync_words(hd)));
       cast = true;
     }
     if (order == ZM_APPLY_THEN_UPDATE) {

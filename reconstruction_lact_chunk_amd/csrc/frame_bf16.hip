@@ -10,10 +10,139 @@
 // their XCD mapping (block index % 8); the apply blocks follow.  Results are
 // those of the two separate kernels, bit for bit: each block runs the same
 // code on the same tokens.
+//
+// For short chunks the launch can also reduce the partial sums (the step and
+// renorm of the review of ZipMap, Method 2, after Eq. (3)).  Reduce blocks
+// come last.  Each waits until every update and apply block of its head has
+// finished, then runs the reduce kernel's per-element code
+// (reduce_rows.h) on its share of the head.  Results again equal the separate
+// kernels bit for bit.  This removes the reduce's launch and, more
+// important, its read of the partial sums from memory: they are written and
+// read inside one XCD's L2.
+//
+// How the wait works.  With heads a multiple of 8, every update and apply
+// block of head j has a block index of j's residue mod 8, and the reduce
+// blocks of head j are placed the same way, so all of them run on one XCD
+// (blocks are dispatched round-robin over the 8 XCDs).  That XCD's L2 is the
+// point where its compute units see each other's stores.  A finishing block
+// waits for its own stores to complete (vmcnt 0: written into the L2), then
+// one thread adds 1 to its head's arrival counter with a device-scope atomic.
+// A reduce block's first thread polls that counter until all of the head's
+// blocks have arrived; its loads of the partial sums come after a workgroup
+// barrier, and no block of the launch has read those addresses before, so
+// none can hit a stale line in a compute unit's L1.  Every block checks the
+// XCD it runs on (the hardware XCC_ID register) against its index: a block
+// off its head's XCD adds a flag to the count, and a reduce block that sees
+// the flag (or runs off its XCD itself) writes NaN rather than a value it
+// cannot trust.
+//
+// Progress.  Update and apply blocks never wait, and reduce blocks have the
+// highest indices, so every block a reduce block waits for is dispatched no
+// later than the reduce block itself and finishes on its own; the reduce
+// blocks also stay fewer than the compute units of an XCD.  The poll is
+// bounded in time all the same (kSpinTicks of the 100 MHz real-time clock,
+// far beyond the longest frame the planner fuses): a reduce block that runs
+// out sets a sticky error word and writes NaN, and so does every later fused
+// launch on this workspace until a cast clears the word.
+//
+// The last reduce block of a head to pass its wait clears the head's
+// counters, so each launch leaves the sync region as it found it (zero).
 #include "apply_bf16.h"
+#include "reduce_rows.h"
 #include "update_bf16.h"
 
 namespace zm {
+
+namespace {
+
+constexpr unsigned kCountBits = 20;          // arrivals in the low bits of a counter
+constexpr unsigned kCountMask = (1u << kCountBits) - 1;
+constexpr unsigned kOffXcd = 1u << kCountBits;  // added by a block off its head's XCD
+constexpr uint64_t kSpinTicks = 50000000;    // 0.5 s of the 100 MHz real-time clock
+constexpr int kRedPerXcd = 24;               // at most this many reduce blocks per XCD
+
+// The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ unsigned hw_xcd() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u;
+}
+
+// Called by every thread of a block once its stores are issued.
+__device__ __forceinline__ void arrive(unsigned* ctr, int blk) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned v = 1u + (hw_xcd() == (unsigned)(blk & 7) ? 0u : kOffXcd);
+    __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Waits for `arrivals` blocks of head hd; true if the reduce may trust the
+// partial sums.  `per_head` reduce blocks wait on each head.  flag: one int
+// of LDS.
+__device__ __forceinline__ bool wait_head(unsigned* sync, int heads, int hd, unsigned arrivals,
+                                          unsigned per_head, int* flag) {
+  if (threadIdx.x == 0) {
+    unsigned* ctr = sync + kSyncWords * hd;
+    unsigned* err = sync + kSyncWords * heads;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned v;
+    bool timeout = false;
+    while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
+            kCountMask) < arrivals) {
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+        timeout = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (timeout) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool ok = !timeout && (v >> kCountBits) == 0 &&
+                    __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
+    // the head's last reduce block past the wait clears its counters
+    if (__hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        per_head - 1) {
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    *flag = ok;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Reduce block rb (0-based, rb % 8 its XCD): items of 2048 weight elements,
+// the P2 items of each head of this XCD in turn, every per_xcd-th one from
+// rb / 8.  per_xcd <= P2, so each of the XCD's reduce blocks waits once on
+// every head of the XCD.  The two halves of the workgroup take the two
+// 1024-element halves of an item (one matrix: h d is a multiple of 2048).
+template <int D, int HID>
+__device__ __forceinline__ void reduce_blocks(int rb, uint16_t* lds, const float* part,
+                                              int splits, int heads, unsigned* sync,
+                                              unsigned arrivals, int per_xcd,
+                                              const ReduceOut& ro) {
+  constexpr int P2 = 3 * HID * D / 2048;
+  constexpr int64_t HD3 = 3 * (int64_t)HID * D;
+  const int xcd = rb & 7, idx = rb >> 3;
+  const int items = (heads / 8) * P2;
+  float* const tr = reinterpret_cast<float*>(lds) + 1024 * (threadIdx.x >> 8);
+  int* const flag = reinterpret_cast<int*>(lds) + 2048;
+  const bool here = hw_xcd() == (unsigned)xcd;
+  bool ok = true;
+  int cur = -1;
+  for (int i = idx; i < items; i += per_xcd) {
+    const int hl = i / P2, hd = xcd + 8 * hl;
+    if (hl != cur) {
+      cur = hl;
+      ok = wait_head(sync, heads, hd, arrivals, (unsigned)per_xcd, flag) && here;
+    }
+    reduce_1k<D, HID>(part, splits, heads,
+                      hd * HD3 + (int64_t)(i - hl * P2) * 2048 + 1024 * (threadIdx.x >> 8),
+                      threadIdx.x & 255, ro, tr, !ok);
+    __syncthreads();  // tr and flag are rewritten for the next item
+  }
+}
+
+}  // namespace
 
 template <int D, int HID, int TG>
 __global__ __launch_bounds__(512) void k_frame_bf16(
@@ -23,23 +152,39 @@ __global__ __launch_bounds__(512) void k_frame_bf16(
     const uint16_t* __restrict__ w1b,
     const uint16_t* __restrict__ w3b, const uint16_t* __restrict__ w2b,
     const uint16_t* __restrict__ w2tb, float* __restrict__ part, int splits, int64_t chunk_u,
-    int upd_blocks, int64_t chunk_a) {
-  constexpr int LU = UpdCfg<D, HID, TG>::LDS_ELEMS, LA = AppCfg<D, HID>::LDS_ELEMS;
+    int upd_blocks, int64_t chunk_a, int app_blocks, unsigned* sync, int red_base,
+    int red_per_xcd, unsigned arrivals, ReduceOut ro) {
+  using UC = UpdCfg<D, HID, TG>;
+  constexpr int LU = UC::LDS_ELEMS, LA = AppCfg<D, HID>::LDS_ELEMS;
+  static_assert(LU >= 2 * 2048 + 2 && LA >= 2 * 2048 + 2, "reduce scratch fits the LDS");
   __shared__ __attribute__((aligned(16))) uint16_t lds[LU > LA ? LU : LA];
-  if ((int)blockIdx.x < upd_blocks)
-    update_tiles<D, HID, false, TG>(blockIdx.x, lds, kp, vp, eta, n_kv, ld, heads, w1b, w3b,
-                                    w2tb, part, splits, chunk_u);
-  else
-    apply_tiles<D, HID>(blockIdx.x - upd_blocks, lds, qp, op, n_q, ld, heads, w1b, w3b, w2b,
-                        chunk_a);
+  const int b = blockIdx.x;
+  if (b < upd_blocks) {
+    update_tiles<D, HID, false, TG>(b, lds, kp, vp, eta, n_kv, ld, heads, w1b, w3b, w2tb, part,
+                                    splits, chunk_u);
+    if (sync) {
+      const int pair = upd_block_pair<UC::NSL>(b);
+      if (pair < heads * splits) arrive(sync + kSyncWords * (pair % heads), b);
+    }
+  } else if (sync == nullptr || b < red_base) {
+    // blocks past the apply's (padding before the reduce blocks) find no tokens
+    apply_tiles<D, HID>(b - upd_blocks, lds, qp, op, n_q, ld, heads, w1b, w3b, w2b, chunk_a);
+    if (sync && b - upd_blocks < app_blocks)
+      arrive(sync + kSyncWords * ((b - upd_blocks) % heads), b);
+  } else {
+    reduce_blocks<D, HID>(b - red_base, lds, part, splits, heads, sync, arrivals, red_per_xcd,
+                          ro);
+  }
 }
 
 hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const uint16_t* k,
                              const uint16_t* v, const float* eta, int64_t n_kv, int64_t ld,
                              int heads, int d, int h, WSet w, float* part, UpdatePlan plan,
-                             hipStream_t st) {
+                             hipStream_t st, const FrameReduce* fr) {
   if (plan.splits <= 0 || n_kv <= 0 || n_q <= 0) return hipErrorInvalidValue;
   if (plan.tg != 1 && plan.tg != 2) return hipErrorInvalidValue;
+  if (fr && (!frame_fuses_reduce(heads, n_kv) || fr->sync == nullptr))
+    return hipErrorInvalidValue;
   const int nsl = plan_slices(plan, h);
   const int64_t pairs = (int64_t)heads * plan.splits;
   const int upd_blocks = (int)(ceil_div(pairs, 8) * 8 * nsl);
@@ -48,11 +193,27 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
   // runs and finish last: then they take the usual plan and queue behind
   // the update's workgroups instead.
   if (ap.chunk > 2 * plan.chunk) ap = plan_apply(n_q, heads);
-  const unsigned blocks = (unsigned)(upd_blocks + (int64_t)heads * ap.splits);
+  const int app_blocks = heads * ap.splits;
+  // Reduce blocks: from the first multiple of 8 after the apply blocks, at
+  // most kRedPerXcd and at most one head's items per XCD.
+  int red_base = upd_blocks + app_blocks, red_per_xcd = 0;
+  unsigned arrivals = 0;
+  ReduceOut ro{};
+  unsigned* sync = nullptr;
+  if (fr) {
+    red_base = (int)(ceil_div(red_base, 8) * 8);
+    const int p2 = 3 * h * d / 2048;
+    red_per_xcd = p2 < kRedPerXcd ? p2 : kRedPerXcd;
+    arrivals = (unsigned)(plan.splits * nsl + ap.splits);
+    ro = fr->out;
+    sync = fr->sync;
+  }
+  const unsigned blocks = (unsigned)(red_base + 8 * red_per_xcd);
 #define ZM_LAUNCH_FRAME_TG(DD, HH, TT)                                                          \
   hipLaunchKernelGGL((k_frame_bf16<DD, HH, TT>), dim3(blocks), dim3(512), 0, st, q, o, n_q, k,  \
                      v, eta, n_kv, ld, heads, w.w1b, w.w3b, w.w2b, w.w2tb, part, plan.splits,    \
-                     plan.chunk, upd_blocks, ap.chunk)
+                     plan.chunk, upd_blocks, ap.chunk, app_blocks, sync, red_base, red_per_xcd,  \
+                     arrivals, ro)
 #define ZM_LAUNCH_FRAME(DD, HH)          \
   do {                                   \
     if (plan.tg == 2)                    \

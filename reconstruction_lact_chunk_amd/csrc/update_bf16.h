@@ -118,6 +118,18 @@ __device__ __forceinline__ void gate_backward(float x, float b, float e, float& 
   ga = e * fmaf(sg, fmaf(kNegLog2e, b, -u), u);
 }
 
+// Block -> (pair, slice) of the update: blocks are dispatched round-robin
+// over the 8 XCDs; the NSL hidden slices of one (head, chunk) pair get ids 8
+// apart, so they run on the same XCD at about the same time and share K/V
+// through its L2.  Pair p is head p % heads of token chunk p / heads; p >=
+// heads * splits marks a block without work.  With heads a multiple of 8,
+// every block of head j has an id of j's residue mod 8.
+template <int NSL>
+__device__ __forceinline__ int upd_block_pair(int blk) {
+  const int xcd = blk & 7, r = blk >> 3;
+  return (r / NSL) * 8 + xcd;
+}
+
 // The work of update block `blk` (one workgroup of 512 threads): the kernels
 // that run it pass their block index (offset so that blk % 8 is still the
 // block's XCD) and a 16-byte-aligned LDS buffer of UpdCfg::LDS_ELEMS elements.
@@ -137,13 +149,8 @@ __device__ __forceinline__ void update_tiles(
   using C = UpdCfg<D, HID, TG>;
   constexpr int T = C::T, KS = C::KS, MB = C::MB, CPT = C::CPT, IPT = C::IPT;
 
-  // Block -> (head, chunk, hidden slice).  Blocks are dispatched round-robin
-  // over the 8 XCDs; the slices of one (head, chunk) get ids 8 apart, so they
-  // run on the same XCD at about the same time and share K/V through its L2.
-  const int b = blk;
-  const int xcd = b & 7, r = b >> 3;
-  const int slice = r % C::NSL;
-  const int pair = (r / C::NSL) * 8 + xcd;
+  const int slice = (blk >> 3) % C::NSL;
+  const int pair = upd_block_pair<C::NSL>(blk);
   if (pair >= heads * splits) return;
   const int head = pair % heads, chunk_id = pair / heads;
   const int64_t t_begin = (int64_t)chunk_id * chunk;

@@ -37,6 +37,21 @@ struct WSet {
   uint16_t* w2tb;  // W2 transposed: [h][d]
 };
 
+// Where a reduce writes the stepped weights: fp32 W' (may alias the inputs w*:
+// every element is read and written by the same thread) and, with emit, its
+// bf16 copies into ob.
+struct ReduceOut {
+  const float* w1;
+  const float* w2;
+  const float* w3;
+  float* o1;
+  float* o2;
+  float* o3;
+  WSet ob;
+  int renorm;
+  int emit;
+};
+
 // Keeps a computed value in place: an empty volatile asm that takes the value
 // as a register in/out operand, so the compiler must compute it before this
 // point and cannot sink the computation towards its later uses.  Emits no
@@ -208,8 +223,9 @@ inline ApplyPlan plan_apply(int64_t n, int heads, int64_t wgs = kTargetWgs) {
 }
 
 // ---- launchers (each returns hipSuccess or the launch error) --------------
+// zero non-null: the same launch also clears nzero words there.
 hipError_t launch_cast(const float* w1, const float* w2, const float* w3, int heads, int d, int h,
-                       WSet out, hipStream_t st);
+                       WSet out, hipStream_t st, unsigned* zero = nullptr, int nzero = 0);
 
 // loss_part non-null: also the virtual loss's per-workgroup sums (splits x
 // heads x plan_slices floats) for launch_loss_sum.
@@ -236,13 +252,34 @@ hipError_t launch_sum_splits(float* part, int splits, int heads, int d, int h, h
 hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t ld, int heads,
                              int d, int h, WSet w, hipStream_t st);
 
+// The reduce inside the shared read-and-update launch (frame_bf16.hip): the
+// launch's last workgroups wait for the update and read workgroups of their
+// head, then reduce its partial sums, which are still in that XCD's L2.  It
+// needs every workgroup of a head on one XCD (heads a multiple of 8) and a
+// wait that ends well within its bound (frames of at most kFuseMaxTokens).
+// The sync region holds kSyncWords words per head and one more block for a
+// sticky error word; it must be zero before the first such launch (launch_cast
+// clears it) and each launch leaves it zero.
+constexpr int kSyncWords = 64;                  // 256 bytes: one head's counters
+constexpr int64_t kFuseMaxTokens = 65536;
+inline size_t frame_sync_words(int heads) { return (size_t)kSyncWords * (heads + 1); }
+inline bool frame_fuses_reduce(int heads, int64_t n_kv) {
+  return heads % 8 == 0 && n_kv > 0 && n_kv <= kFuseMaxTokens;
+}
+struct FrameReduce {
+  unsigned* sync;   // frame_sync_words(heads) words
+  ReduceOut out;
+};
+
 // The apply of n_q queries and the update partial sums over n_kv tokens
 // (plan = plan_update(n_kv, ...)), both through the bf16 set w, in one launch
 // (frame_bf16.hip).  n_q, n_kv > 0; q / o and k / v rows share the stride ld.
+// fr non-null (frame_fuses_reduce must hold): the launch also reduces the
+// partial sums into fr->out, as launch_reduce would.
 hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const uint16_t* k,
                              const uint16_t* v, const float* eta, int64_t n_kv, int64_t ld,
                              int heads, int d, int h, WSet w, float* part, UpdatePlan plan,
-                             hipStream_t st);
+                             hipStream_t st, const FrameReduce* fr = nullptr);
 
 hipError_t launch_update_f32(const float* k, const float* v, const float* eta, int64_t n,
                              int64_t ld, int heads, int d, int h, const float* w1,

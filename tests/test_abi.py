@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert zm.version() == 10301
+    assert zm.version() == 10400
     assert zm.status_string(0) == "ok"
     for s in (-1, -2, -3, -4):
         assert zm.status_string(s) not in ("ok", "unknown status")
@@ -64,7 +64,9 @@ def test_workspace_size_structure():
     st0, base = ws_size(de, 0, 0)
     assert st0 == 0
     welems = 8 * 256 * 128
-    assert base == 2 * 4 * welems * 2        # two bf16 weight sets, no partial sums
+    # two bf16 weight sets and the shared launch's sync words (256 bytes per
+    # head and one more block), no partial sums
+    assert base == 2 * 4 * welems * 2 + 256 * (8 + 1)
     st, big = ws_size(de, 961_800, 961_800)
     assert st == 0
     # the partial-sum slots (3 h d fp32 per head each), then one fp32 per

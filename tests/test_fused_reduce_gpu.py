@@ -1,0 +1,150 @@
+"""The reduce inside the shared read-and-update launch (frame_bf16.hip).
+
+For heads a multiple of 8 and frames of at most 65,536 tokens, the launch that
+reads a frame and computes its partial sums also reduces them: its last
+workgroups wait on per-head arrival counters in the workspace, then run the
+reduce kernel's code.  These tests hold it to the separate kernels bit for bit.
+The cases cover every narrow shape, 8 to 64 heads, ragged and single-tile
+frames, both update shapes (short frames take two token groups, 65,536 tokens
+take one), and the first frame past the limit, which takes the separate reduce.
+The counters must be zero after every launch.  A sticky error word set from
+the host must turn the stepped weights into NaN rather than plausible values.
+"""
+import pytest
+import torch
+
+import reconstruction_lact_chunk_amd as zm
+import workloads as WL
+from test_parity_gpu import say
+
+pytestmark = pytest.mark.gpu
+
+FUSE_MAX = 65536
+
+
+def tensors(n, heads, d, h, seed):
+    q = WL.make_tokens(n, heads, d, "bf16", seed, "cuda", 1)
+    k = WL.make_tokens(n, heads, d, "bf16", seed, "cuda", 2)
+    v = WL.make_tokens(n, heads, d, "bf16", seed, "cuda", 3)
+    eta = WL.make_eta(n, heads, seed, "cuda", eta_scale=20.0)
+    return q, k, v, eta, WL.make_weights(heads, d, h, seed, "cuda")
+
+
+def sync_range(heads, d, h):
+    """Byte range of the sync words in the workspace: after two bf16 weight
+    sets (4 arrays of heads x h x d each, 256-byte rounded)."""
+    set_bytes = (4 * heads * h * d * 2 + 255) // 256 * 256
+    return 2 * set_bytes, 2 * set_bytes + 256 * (heads + 1)
+
+
+def workspace(w, q, n):
+    desc = zm.make_desc(*w, zm.BF16, True, q, q)
+    return torch.zeros(zm.workspace_size(desc, n, n), dtype=torch.uint8, device="cuda")
+
+
+@pytest.mark.parametrize("heads,d,h,n", [
+    (8, 128, 256, 1374),       # the streamed frame
+    (8, 128, 256, 33),         # one ragged tile
+    (16, 128, 128, 2000),
+    (8, 64, 128, 500),         # 12 reduce blocks per XCD (a head's items)
+    (24, 64, 256, 4000),       # three heads per XCD
+    (64, 64, 128, 1374),       # eight heads per XCD
+    (8, 128, 256, FUSE_MAX),   # the longest fused frame (one token group)
+    (8, 128, 256, FUSE_MAX + 1),   # separate reduce
+])
+def test_fused_reduce_equals_separate_kernels(heads, d, h, n):
+    say(f"case fused reduce H={heads} d={d} h={h} n={n}")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=71 + heads + n % 13)
+    state = [t.clone() for t in w]
+    ws = workspace(w, q, n)
+    o = zm.stream_step(q, k, v, eta, *state, renorm=True, order=zm.APPLY_THEN_UPDATE,
+                       workspace=ws)
+    o_ref = zm.apply(q, *w)
+    w_ref = zm.update(k, v, eta, *w, renorm=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in zip(state, w_ref):
+        assert torch.equal(a, b)
+    a, b = sync_range(heads, d, h)
+    assert int(ws[a:b].count_nonzero()) == 0
+
+
+@pytest.mark.parametrize("renorm", [True, False])
+def test_emitting_chain_equals_separate_calls(renorm):
+    """Frames that keep W's bf16 copies in the workspace (the reduce blocks
+    write them while other heads' blocks still read theirs) against a plain
+    loop of zm_ttt_apply / zm_ttt_update."""
+    heads, d, h = 8, 128, 256
+    sizes = [1374, 1001, 33, 1374, 4096]
+    n = sum(sizes)
+    say(f"case fused reduce emitting chain renorm={renorm}")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=77)
+    state = [t.clone() for t in w]
+    ref = [t.clone() for t in w]
+    ws = workspace(w, q, max(sizes))
+    s = 0
+    for i, m in enumerate(sizes):
+        sl = slice(s, s + m)
+        o = zm.stream_step(q[sl], k[sl], v[sl], eta[sl], *state, renorm=renorm, workspace=ws,
+                           emit_bf16=True, reuse_bf16=i > 0)
+        o_ref = zm.apply(q[sl], *ref)
+        ref = list(zm.update(k[sl], v[sl], eta[sl], *ref, renorm=renorm))
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), i
+        for a, b in zip(state, ref):
+            assert torch.equal(a, b), i
+        s += m
+    a, b = sync_range(heads, d, h)
+    assert int(ws[a:b].count_nonzero()) == 0
+
+
+def test_sticky_error_word_gives_nan_until_a_cast_clears_it():
+    heads, d, h, n = 8, 128, 256, 1374
+    say("case fused reduce sticky error word")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=79)
+    state = [t.clone() for t in w]
+    ws = workspace(w, q, n)
+    zm.stream_step(q, k, v, eta, *state, renorm=True, workspace=ws, emit_bf16=True)
+    a, _ = sync_range(heads, d, h)
+    err = a + 256 * heads
+    ws[err] = 1   # as a timed-out wait would leave it
+    prev = [t.clone() for t in state]
+    o = zm.stream_step(q, k, v, eta, *state, renorm=True, workspace=ws, emit_bf16=True,
+                       reuse_bf16=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, zm.apply(q, *prev))       # the read still used the incoming W
+    for t in state:
+        assert bool(torch.isnan(t).all())
+    assert int(ws[err]) == 1                         # sticky
+    # a call that casts clears the word: fresh weights give the separate result again
+    state = [t.clone() for t in w]
+    zm.stream_step(q, k, v, eta, *state, renorm=True, workspace=ws)
+    w_ref = zm.update(k, v, eta, *w, renorm=True)
+    torch.cuda.synchronize()
+    for x, y in zip(state, w_ref):
+        assert torch.equal(x, y)
+    assert int(ws[err]) == 0
+
+
+def test_chunked_block_causal_fuses_every_step():
+    """zm_ttt_chunked in the block-causal order pairs chunk c's read with its
+    update in one launch; with 8 heads every such step reduces inside it."""
+    heads, d, h = 8, 128, 256
+    offsets = [0, 1374, 2748, 2781, 4122, 4122, 5496]
+    n = offsets[-1]
+    say("case fused reduce chunked block-causal")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=81)
+    state = [t.clone() for t in w]
+    o = zm.chunked(q, k, v, eta, offsets, *state, renorm=True, order=zm.APPLY_THEN_UPDATE)
+    ref = [t.clone() for t in w]
+    o_ref = torch.zeros_like(o)
+    for c in range(len(offsets) - 1):
+        s, e = offsets[c], offsets[c + 1]
+        if s == e:
+            continue
+        o_ref[s:e] = zm.apply(q[s:e], *ref)
+        ref = list(zm.update(k[s:e], v[s:e], eta[s:e], *ref, renorm=True))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in zip(state, ref):
+        assert torch.equal(a, b)

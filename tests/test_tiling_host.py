@@ -691,3 +691,96 @@ def test_reserved_slots_cover_every_shorter_update(heads, d_hidden):
     if (heads, d_hidden) == (16, 256):
         assert realized_drops
         assert plan_update(1058, 16, 256)[0] == 7 and plan_update(949, 16, 256)[0] == 8
+
+
+# ---- the reduce inside the shared read-and-update launch (frame_bf16.hip) ----
+
+FUSE_MAX = 65536
+RED_PER_XCD = 24
+
+
+def plan_apply_wgs(n, heads, wgs):
+    """plan_apply with a workgroup budget (the compute units the update leaves)."""
+    if n <= 0:
+        return 0, 0
+    if wgs < heads:
+        wgs = TARGET_WGS
+    target = max(wgs // heads, 1)
+    tiles = ceil_div(n, TOK)
+    s = min(tiles, target)
+    chunk = ceil_div(tiles, s) * TOK
+    return ceil_div(n, chunk), chunk
+
+
+def frame_blocks(n, heads, d, h):
+    """The block roles of a fused frame launch: (signalling blocks as
+    (block, head), reduce blocks as (block, [(head, first element)]),
+    arrivals per head, reduce blocks per XCD)."""
+    splits, chunk, tg = plan_update_tg(n, heads, h)
+    nsl = h // (128 // tg)
+    pairs = heads * splits
+    upd_blocks = ceil_div(pairs, 8) * 8 * nsl
+    ap_splits, ap_chunk = plan_apply_wgs(n, heads, TARGET_WGS - upd_blocks)
+    if ap_chunk > 2 * chunk:
+        ap_splits, ap_chunk = plan_apply(n, heads)
+    app_blocks = heads * ap_splits
+    red_base = ceil_div(upd_blocks + app_blocks, 8) * 8
+    p2 = 3 * h * d // 2048
+    per_xcd = min(p2, RED_PER_XCD)
+    signal = []
+    for b in range(upd_blocks):
+        pair = ((b >> 3) // nsl) * 8 + (b & 7)
+        if pair < pairs:
+            signal.append((b, pair % heads))
+    for b in range(upd_blocks, red_base):
+        ab = b - upd_blocks
+        if ab < app_blocks:
+            assert (ab // heads) * ap_chunk < n          # a block with tokens
+            signal.append((b, ab % heads))
+        else:
+            assert (ab // heads) * ap_chunk >= n         # padding finds no tokens
+    reduce = []
+    for b in range(red_base, red_base + 8 * per_xcd):
+        rb = b - red_base
+        xcd, idx = rb & 7, rb >> 3
+        work = []
+        for i in range(idx, (heads // 8) * p2, per_xcd):
+            hl = i // p2
+            hd = xcd + 8 * hl
+            work.append((hd, hd * 3 * h * d + (i - hl * p2) * 2048))
+        reduce.append((b, work))
+    return signal, reduce, splits * nsl + ap_splits, per_xcd
+
+
+@pytest.mark.parametrize("heads,d,h", [(8, 128, 256), (8, 128, 128), (8, 64, 256), (8, 64, 128),
+                                       (16, 128, 256), (24, 64, 256), (64, 64, 128),
+                                       (64, 128, 256)])
+@pytest.mark.parametrize("n", [1, 33, 500, 1374, 4000, 20_000, FUSE_MAX])
+def test_fused_reduce_blocks(heads, d, h, n):
+    signal, reduce, arrivals, per_xcd = frame_blocks(n, heads, d, h)
+    assert per_xcd < 32                                # fewer than an XCD's compute units
+    # every signalling block runs on its head's XCD and each head counts
+    # exactly the arrivals its reduce blocks wait for
+    count = [0] * heads
+    for b, hd in signal:
+        assert b % 8 == hd % 8
+        count[hd] += 1
+    assert count == [arrivals] * heads
+    # reduce blocks: on their heads' XCD, each weight element exactly once,
+    # both halves of an item in one matrix, per_xcd blocks waiting per head
+    HD = h * d
+    seen = np.zeros(heads * 3 * HD, dtype=np.int32)
+    waiters = [0] * heads
+    for b, work in reduce:
+        heads_here = []
+        for hd, e0 in work:
+            assert b % 8 == hd % 8
+            assert e0 % 2048 == 0 and (e0 % (3 * HD)) // HD == (e0 % (3 * HD) + 2047) // HD
+            seen[e0:e0 + 2048] += 1
+            if not heads_here or heads_here[-1] != hd:
+                heads_here.append(hd)
+        assert len(heads_here) == len(set(heads_here))   # one wait per head
+        for hd in heads_here:
+            waiters[hd] += 1
+    assert (seen == 1).all()
+    assert waiters == [per_xcd] * heads
