@@ -4,9 +4,9 @@
 // schedules of the LaCT summary (mhpn.cn, part 二, 3、应用场景) have such
 // pairs: a chunk read before it is written (order (c), the default streaming
 // frame: the same chunk's q and k), and in the block-causal order (b) the
-// read of chunk c after its update together with the update of chunk c + 1.  This saves a launch and lets the
-// shorter read fill the compute units the update leaves free, instead of
-// running after it.  Update blocks come first (they take longer) and keep
+// read of chunk c after its update together with the update of chunk c + 1.
+// This saves a launch and lets the shorter read fill the compute units the
+// update leaves free, instead of running after it.  Update blocks come first (they take longer) and keep
 // their XCD mapping (block index % 8); the apply blocks follow.  Results are
 // those of the two separate kernels, bit for bit: each block runs the same
 // code on the same tokens.
@@ -16,18 +16,20 @@
 // come last.  Each waits until every update and apply block of its head has
 // finished, then runs the reduce kernel's per-element code
 // (reduce_rows.h) on its share of the head.  Results again equal the separate
-// kernels bit for bit.  This removes the reduce's launch and, more
-// important, its read of the partial sums from memory: they are written and
-// read inside one XCD's L2.
+// kernels bit for bit.  This removes the reduce's launch and the wait between
+// the two launches; the partial sums are written and read back within one
+// XCD, where most of the reads hit its L2.
 //
 // How the wait works.  With heads a multiple of 8, every update and apply
 // block of head j has a block index of j's residue mod 8, and the reduce
 // blocks of head j are placed the same way, so all of them run on one XCD
 // (blocks are dispatched round-robin over the 8 XCDs).  That XCD's L2 is the
-// point where its compute units see each other's stores.  A finishing block
-// waits for its own stores to complete (vmcnt 0: written into the L2), then
-// one thread adds 1 to its head's arrival counter with a device-scope atomic.
-// A reduce block's first thread polls that counter until all of the head's
+// point where its compute units see each other's stores.  A finishing update
+// block waits for its own stores to complete (vmcnt 0: written into the L2),
+// then one thread adds 1 to its head's arrival counter with a device-scope
+// atomic; a read block only has to be past its reads of W (the bf16 copies
+// that the reduce may rewrite), which its results already depend on.  A
+// reduce block's first thread polls that counter until all of the head's
 // blocks have arrived; its loads of the partial sums come after a workgroup
 // barrier, and no block of the launch has read those addresses before, so
 // none can hit a stale line in a compute unit's L1.  Every block checks the
@@ -45,8 +47,15 @@
 // out sets a sticky error word and writes NaN, and so does every later fused
 // launch on this workspace until a cast clears the word.
 //
-// The last reduce block of a head to pass its wait clears the head's
-// counters, so each launch leaves the sync region as it found it (zero).
+// Each reduce block counts itself past the wait in a second word of its
+// head; the last one to count clears both words once its own items are
+// done, so each launch leaves the sync region as it found it (zero).
+//
+// Measured on 1374-token frames (8 heads of 128 / 256): the reduce blocks
+// read about 86% of their requests from the L2, yet the launch fetches as
+// many bytes from memory as the two separate launches did (the W rows and
+// the partial sums the L2 could not keep); the gain is the reduce's launch
+// and the wait between the launches, about 2.5 us of a 28 us frame.
 #include "apply_bf16.h"
 #include "reduce_rows.h"
 #include "update_bf16.h"
@@ -60,15 +69,19 @@ constexpr unsigned kCountMask = (1u << kCountBits) - 1;
 constexpr unsigned kOffXcd = 1u << kCountBits;  // added by a block off its head's XCD
 constexpr uint64_t kSpinTicks = 50000000;    // 0.5 s of the 100 MHz real-time clock
 constexpr int kRedPerXcd = 24;               // at most this many reduce blocks per XCD
+constexpr int kRedU = 2;                     // items a reduce block loads at once
 
 // The XCD this wave runs on (hardware register XCC_ID, bits 3:0).
 __device__ __forceinline__ unsigned hw_xcd() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u;
 }
 
-// Called by every thread of a block once its stores are issued.
-__device__ __forceinline__ void arrive(unsigned* ctr, int blk) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Called by every thread of a block at its end.  stores: the block's global
+// stores must be in the L2 before the count (update blocks: the partial
+// sums); a read block only has to be past its reads of W, which its results
+// already depend on.
+__device__ __forceinline__ void arrive(unsigned* ctr, int blk, bool stores) {
+  if (stores) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned v = 1u + (hw_xcd() == (unsigned)(blk & 7) ? 0u : kOffXcd);
@@ -76,14 +89,14 @@ __device__ __forceinline__ void arrive(unsigned* ctr, int blk) {
   }
 }
 
-// Waits for `arrivals` blocks of head hd; true if the reduce may trust the
-// partial sums.  `per_head` reduce blocks wait on each head.  flag: one int
-// of LDS.
-__device__ __forceinline__ bool wait_head(unsigned* sync, int heads, int hd, unsigned arrivals,
-                                          unsigned per_head, int* flag) {
+// Thread 0 polls the head's arrival counter until `arrivals` blocks have
+// counted; true if the reduce may trust the partial sums (no time-out, no
+// block off its XCD, no sticky error from an earlier launch: sticky_ok).
+// flag: one int of LDS.  No global memory wait comes after the poll, so the
+// caller's loads issue at once.
+__device__ __forceinline__ bool wait_head(unsigned* ctr, unsigned* err, unsigned arrivals,
+                                          bool sticky_ok, int* flag) {
   if (threadIdx.x == 0) {
-    unsigned* ctr = sync + kSyncWords * hd;
-    unsigned* err = sync + kSyncWords * heads;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     unsigned v;
     bool timeout = false;
@@ -96,15 +109,7 @@ __device__ __forceinline__ bool wait_head(unsigned* sync, int heads, int hd, uns
       __builtin_amdgcn_s_sleep(2);
     }
     if (timeout) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool ok = !timeout && (v >> kCountBits) == 0 &&
-                    __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
-    // the head's last reduce block past the wait clears its counters
-    if (__hip_atomic_fetch_add(ctr + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-        per_head - 1) {
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    *flag = ok;
+    *flag = !timeout && (v >> kCountBits) == 0 && sticky_ok;
   }
   __syncthreads();
   return *flag != 0;
@@ -115,31 +120,70 @@ __device__ __forceinline__ bool wait_head(unsigned* sync, int heads, int hd, uns
 // rb / 8.  per_xcd <= P2, so each of the XCD's reduce blocks waits once on
 // every head of the XCD.  The two halves of the workgroup take the two
 // 1024-element halves of an item (one matrix: h d is a multiple of 2048).
+// Items go in groups of up to U of one head: W for a group is loaded before
+// the head's wait and the partial sums of the whole group after it, all
+// loads in flight together.  After the wait thread 0 counts the block as
+// past it; the head's last block to count clears the head's counters once
+// its own items are done (every block of the head is past its wait by then).
 template <int D, int HID>
 __device__ __forceinline__ void reduce_blocks(int rb, uint16_t* lds, const float* part,
                                               int splits, int heads, unsigned* sync,
                                               unsigned arrivals, int per_xcd,
-                                              const ReduceOut& ro) {
+                                              ReduceOut ro) {
+  constexpr int U = kRedU;
   constexpr int P2 = 3 * HID * D / 2048;
   constexpr int64_t HD3 = 3 * (int64_t)HID * D;
   const int xcd = rb & 7, idx = rb >> 3;
   const int items = (heads / 8) * P2;
-  float* const tr = reinterpret_cast<float*>(lds) + 1024 * (threadIdx.x >> 8);
-  int* const flag = reinterpret_cast<int*>(lds) + 2048;
+  // a wave lies in one half: its half index is a scalar
+  const int half = __builtin_amdgcn_readfirstlane(threadIdx.x >> 8), t = threadIdx.x & 255;
+  float* const tr = reinterpret_cast<float*>(lds) + 1024 * half;  // U x 2 x 1024 floats
+  int* const flag = reinterpret_cast<int*>(lds) + 2048 * U;
+  unsigned* const err = sync + kSyncWords * heads;
   const bool here = hw_xcd() == (unsigned)xcd;
+  bool sticky_ok = true;
+  if (threadIdx.x == 0)
+    sticky_ok = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
   bool ok = true;
   int cur = -1;
-  for (int i = idx; i < items; i += per_xcd) {
-    const int hl = i / P2, hd = xcd + 8 * hl;
-    if (hl != cur) {
-      cur = hl;
-      ok = wait_head(sync, heads, hd, arrivals, (unsigned)per_xcd, flag) && here;
+  unsigned passed = 0;  // thread 0: blocks of the current head past the wait before this one
+  auto finish_head = [&](int hl) {
+    if (threadIdx.x == 0 && passed == (unsigned)per_xcd - 1) {
+      unsigned* ctr = sync + kSyncWords * (xcd + 8 * hl);
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    reduce_1k<D, HID>(part, splits, heads,
-                      hd * HD3 + (int64_t)(i - hl * P2) * 2048 + 1024 * (threadIdx.x >> 8),
-                      threadIdx.x & 255, ro, tr, !ok);
-    __syncthreads();  // tr and flag are rewritten for the next item
+  };
+  for (int i = idx; i < items;) {
+    const int hl = i / P2, hd = xcd + 8 * hl;
+    int nu = 1;  // items of this head in the group: i, i + per_xcd, ...
+    while (nu < U && i + nu * per_xcd < items && (i + nu * per_xcd) / P2 == hl) ++nu;
+    RowPos p[U];
+    f32x4 wv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // unused slots repeat item i (loaded, not used)
+      const int j = u < nu ? i + u * per_xcd : i;
+      p[u] = row_pos<D, HID>(hd * HD3 + (int64_t)(j - hl * P2) * 2048 + 1024 * half, t);
+      wv[u] = load_w(p[u], ro);
+    }
+    if (hl != cur) {
+      if (cur >= 0) finish_head(cur);
+      cur = hl;
+      unsigned* ctr = sync + kSyncWords * hd;
+      ok = wait_head(ctr, err, arrivals, sticky_ok, flag) && here;
+      if (threadIdx.x == 0) {
+        // The lane index (0 here) keeps the address lane-varying to the
+        // compiler: a uniform one gets a wave-wide scan around the atomic
+        // that waits for its result at once, while only finish_head needs it.
+        unsigned* done = ctr + 1 + __builtin_amdgcn_mbcnt_lo(~0u, 0u);
+        passed = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    reduce_groups<D, HID, U>(part, splits, heads, p, wv, nu, t, ro, tr, 2048, !ok);
+    __syncthreads();  // tr and flag are rewritten for the next group
+    i += nu * per_xcd;
   }
+  if (cur >= 0) finish_head(cur);
 }
 
 }  // namespace
@@ -156,7 +200,8 @@ __global__ __launch_bounds__(512) void k_frame_bf16(
     int red_per_xcd, unsigned arrivals, ReduceOut ro) {
   using UC = UpdCfg<D, HID, TG>;
   constexpr int LU = UC::LDS_ELEMS, LA = AppCfg<D, HID>::LDS_ELEMS;
-  static_assert(LU >= 2 * 2048 + 2 && LA >= 2 * 2048 + 2, "reduce scratch fits the LDS");
+  static_assert(sizeof(uint16_t) * (LU > LA ? LU : LA) >= sizeof(float) * (2048 * kRedU + 1),
+                "reduce scratch fits the LDS");
   __shared__ __attribute__((aligned(16))) uint16_t lds[LU > LA ? LU : LA];
   const int b = blockIdx.x;
   if (b < upd_blocks) {
@@ -164,13 +209,13 @@ __global__ __launch_bounds__(512) void k_frame_bf16(
                                     splits, chunk_u);
     if (sync) {
       const int pair = upd_block_pair<UC::NSL>(b);
-      if (pair < heads * splits) arrive(sync + kSyncWords * (pair % heads), b);
+      if (pair < heads * splits) arrive(sync + kSyncWords * (pair % heads), b, true);
     }
   } else if (sync == nullptr || b < red_base) {
     // blocks past the apply's (padding before the reduce blocks) find no tokens
     apply_tiles<D, HID>(b - upd_blocks, lds, qp, op, n_q, ld, heads, w1b, w3b, w2b, chunk_a);
     if (sync && b - upd_blocks < app_blocks)
-      arrive(sync + kSyncWords * ((b - upd_blocks) % heads), b);
+      arrive(sync + kSyncWords * ((b - upd_blocks) % heads), b, false);
   } else {
     reduce_blocks<D, HID>(b - red_base, lds, part, splits, heads, sync, arrivals, red_per_xcd,
                           ro);

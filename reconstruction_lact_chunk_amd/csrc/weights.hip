@@ -65,7 +65,9 @@ template <int D, int HID>
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ part, int splits,
                                                 int heads, ReduceOut r) {
   __shared__ float tr[1024];
-  reduce_1k<D, HID>(part, splits, heads, 1024 * (int64_t)blockIdx.x, threadIdx.x, r, tr);
+  const RowPos p[1] = {row_pos<D, HID>(1024 * (int64_t)blockIdx.x, threadIdx.x)};
+  const f32x4 wv[1] = {load_w(p[0], r)};
+  reduce_groups<D, HID, 1>(part, splits, heads, p, wv, 1, threadIdx.x, r, tr, 1024);
 }
 
 hipError_t launch_reduce(const float* part, int splits, int heads, int d, int h,
