@@ -261,13 +261,26 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
   ZM_TRY(check_part_range(L.part, L.plan.splits, welems, wsp.bytes));
   // the virtual loss's block sums (bf16 narrow path only; the entry point checks)
   float* const loss_part = loss ? (float*)((char*)ws + L.loss) : nullptr;
+  unsigned* const sync = (unsigned*)((char*)ws + L.sync);
   if (n > 0) {
     if (d->io_dtype == ZM_BF16) {
       if (!cast_done) {
         Scoped s(kStageCast, st);
-        ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st));
+        ZM_HIP(launch_cast(w1, w2, w3, d->heads, d->d_head, d->d_hidden, a, st, sync,
+                           (int)frame_sync_words(d->heads)));
       }
       Scoped s(kStageUpdate, st);
+      if (!loss && d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, n)) {
+        // short chunk: partial sums and reduce in one launch
+        Scoped r(kStageReduce, st);
+        const FrameReduce fr{sync, ReduceOut{w1, w2, w3, o1, o2, o3,
+                                             emit ? *emit : WSet{nullptr, nullptr, nullptr, nullptr},
+                                             d->renorm, emit ? 1 : 0}};
+        ZM_HIP(launch_frame_bf16(nullptr, nullptr, 0, (const uint16_t*)k, (const uint16_t*)v, eta,
+                                 n, d->ld_tok, d->heads, d->d_head, d->d_hidden, a, part, L.plan,
+                                 st, &fr));
+        return ZM_OK;
+      }
       ZM_HIP(launch_update_bf16((const uint16_t*)k, (const uint16_t*)v, eta, n, d->ld_tok,
                                 d->heads, d->d_head, d->d_hidden, a, part, L.plan, st, loss_part));
     } else {
@@ -425,8 +438,8 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
     const UpdatePlan plan = plan_update(len(c), hd, hh);
     ZM_TRY(check_part_range(L0.part, plan.splits, (size_t)hd * hh * dh, ws.bytes));
     const float* e = eta + offsets[c] * hd;
-    const bool fuse = rc >= 0 && d->step_rule == ZM_STEP_GRADIENT &&
-                      frame_fuses_reduce(hd, len(c));
+    const bool fusable = d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(hd, len(c));
+    const bool fuse = rc >= 0 && fusable, fuse_alone = rc < 0 && fusable;
     {
       Scoped su(kStageUpdate, st);
       if (rc >= 0) {
@@ -435,12 +448,16 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
         ZM_HIP(launch_frame_bf16(tok(q, rc), (uint16_t*)(o + offsets[rc] * row), len(rc), tok(k, c),
                                  tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part, plan, st,
                                  fuse ? &fr : nullptr));
+      } else if (fuse_alone) {
+        const FrameReduce fr{sync, ReduceOut{w1, w2, w3, w1, w2, w3, a, d->renorm, 1}};
+        ZM_HIP(launch_frame_bf16(nullptr, nullptr, 0, tok(k, c), tok(v, c), e, len(c), d->ld_tok,
+                                 hd, dh, hh, a, part, plan, st, &fr));
       } else {
         ZM_HIP(launch_update_bf16(tok(k, c), tok(v, c), e, len(c), d->ld_tok, hd, dh, hh, a, part,
                                   plan, st));
       }
     }
-    if (fuse) return ZM_OK;
+    if (fuse || fuse_alone) return ZM_OK;
     return finish_update(d, len(c), w1, w2, w3, w1, w2, w3, part, plan.splits, &a, st);
   };
   bool cast = false;

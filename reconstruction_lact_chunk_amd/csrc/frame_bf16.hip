@@ -6,10 +6,11 @@
 // frame: the same chunk's q and k), and in the block-causal order (b) the
 // read of chunk c after its update together with the update of chunk c + 1.
 // This saves a launch and lets the shorter read fill the compute units the
-// update leaves free, instead of running after it.  Update blocks come first (they take longer) and keep
-// their XCD mapping (block index % 8); the apply blocks follow.  Results are
-// those of the two separate kernels, bit for bit: each block runs the same
-// code on the same tokens.
+// update leaves free, instead of running after it.  Update blocks come
+// first (they take longer) and keep their block indices, so their XCD
+// grouping (indices that agree mod 8 share an XCD) is that of the update
+// kernel; the apply blocks follow.  Results are those of the two separate
+// kernels, bit for bit: each block runs the same code on the same tokens.
 //
 // For short chunks the launch can also reduce the partial sums (the step and
 // renorm of the review of ZipMap, Method 2, after Eq. (3)).  Reduce blocks
@@ -20,22 +21,29 @@
 // the two launches; the partial sums are written and read back within one
 // XCD, where most of the reads hit its L2.
 //
-// How the wait works.  With heads a multiple of 8, every update and apply
-// block of head j has a block index of j's residue mod 8, and the reduce
-// blocks of head j are placed the same way, so all of them run on one XCD
-// (blocks are dispatched round-robin over the 8 XCDs).  That XCD's L2 is the
-// point where its compute units see each other's stores.  A finishing update
-// block waits for its own stores to complete (vmcnt 0: written into the L2),
-// then one thread adds 1 to its head's arrival counter with a device-scope
-// atomic; a read block only has to be past its reads of W (the bf16 copies
-// that the reduce may rewrite), which its results already depend on.  A
-// reduce block's first thread polls that counter until all of the head's
-// blocks have arrived; its loads of the partial sums come after a workgroup
-// barrier, and no block of the launch has read those addresses before, so
-// none can hit a stale line in a compute unit's L1.  Every block checks the
-// XCD it runs on (the hardware XCC_ID register) against its index: a block
-// off its head's XCD adds a flag to the count, and a reduce block that sees
-// the flag (or runs off its XCD itself) writes NaN rather than a value it
+// How the wait works.  Blocks are dispatched round-robin over the 8 XCDs:
+// block b runs on XCD (b + s) mod 8, where the offset s is the same for every
+// block of a launch but changes from launch to launch (it continues from the
+// launches before; measured with eager launches and graph replays alike).
+// With heads a multiple of 8, every update and apply block of head j has a
+// block index of j's residue mod 8, and the reduce blocks of head j are
+// placed the same way, so all of them run on one XCD, whatever s is.  That
+// XCD's L2 is the point where its compute units see each other's stores.  A
+// finishing update block waits for its own stores to complete (vmcnt 0:
+// written into the L2), then one thread adds to its head's arrival counter
+// with a device-scope atomic; a read block only has to be past its reads of
+// W (the bf16 copies that the reduce may rewrite), which its results already
+// depend on.  A reduce block's first thread polls that counter until all of
+// the head's blocks have arrived; its loads of the partial sums come after a
+// workgroup barrier, and no block of the launch has read those addresses
+// before, so none can hit a stale line in a compute unit's L1.
+//
+// The one-XCD premise is checked, not assumed.  Every block reads the XCD it
+// runs on (the hardware XCC_ID register) and derives its offset s; the
+// arrival counter is 64 bits with one 8-bit field per offset, and a block
+// adds 1 to its own offset's field.  A reduce block trusts the partial sums
+// only if every arrival of its head sits in the field of its own offset
+// (then all ran on its XCD); otherwise it writes NaN rather than a value it
 // cannot trust.
 //
 // Progress.  Update and apply blocks never wait, and reduce blocks have the
@@ -47,9 +55,10 @@
 // out sets a sticky error word and writes NaN, and so does every later fused
 // launch on this workspace until a cast clears the word.
 //
-// Each reduce block counts itself past the wait in a second word of its
-// head; the last one to count clears both words once its own items are
-// done, so each launch leaves the sync region as it found it (zero).
+// Each reduce block counts itself past the wait in another word of its
+// head; the last one to count clears the counter and that word once its own
+// items are done, so each launch leaves the sync region as it found it
+// (zero).
 //
 // Measured on 1374-token frames (8 heads of 128 / 256): the reduce blocks
 // read about 86% of their requests from the L2, yet the launch fetches as
@@ -64,9 +73,9 @@ namespace zm {
 
 namespace {
 
-constexpr unsigned kCountBits = 20;          // arrivals in the low bits of a counter
-constexpr unsigned kCountMask = (1u << kCountBits) - 1;
-constexpr unsigned kOffXcd = 1u << kCountBits;  // added by a block off its head's XCD
+// Arrival counter of a head: the first 64 bits of its kSyncWords block, 8
+// bits per dispatch offset; word 2 counts the reduce blocks past the wait.
+constexpr unsigned kMaxArrivals = 255;
 constexpr uint64_t kSpinTicks = 50000000;    // 0.5 s of the 100 MHz real-time clock
 constexpr int kRedPerXcd = 24;               // at most this many reduce blocks per XCD
 constexpr int kRedU = 2;                     // items a reduce block loads at once
@@ -76,6 +85,19 @@ __device__ __forceinline__ unsigned hw_xcd() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | (3 << 11)) & 7u;
 }
 
+// This launch's dispatch offset as seen by block blk: XCD = (blk + s) mod 8.
+__device__ __forceinline__ unsigned dispatch_offset(int blk) {
+  return (hw_xcd() - (unsigned)blk) & 7u;
+}
+
+// Sum of the 8 one-byte fields of an arrival counter.
+__device__ __forceinline__ unsigned field_sum(unsigned long long v) {
+  unsigned t = 0;
+#pragma unroll
+  for (int f = 0; f < 8; ++f) t += (unsigned)(v >> (8 * f)) & 0xffu;
+  return t;
+}
+
 // Called by every thread of a block at its end.  stores: the block's global
 // stores must be in the L2 before the count (update blocks: the partial
 // sums); a read block only has to be past its reads of W, which its results
@@ -83,25 +105,27 @@ __device__ __forceinline__ unsigned hw_xcd() {
 __device__ __forceinline__ void arrive(unsigned* ctr, int blk, bool stores) {
   if (stores) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned v = 1u + (hw_xcd() == (unsigned)(blk & 7) ? 0u : kOffXcd);
-    __hip_atomic_fetch_add(ctr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(reinterpret_cast<unsigned long long*>(ctr),
+                           1ull << (8 * dispatch_offset(blk)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Thread 0 polls the head's arrival counter until `arrivals` blocks have
-// counted; true if the reduce may trust the partial sums (no time-out, no
-// block off its XCD, no sticky error from an earlier launch: sticky_ok).
-// flag: one int of LDS.  No global memory wait comes after the poll, so the
-// caller's loads issue at once.
+// counted; true if the reduce may trust the partial sums: no time-out, every
+// arrival from the dispatch offset `offset` of this block (so from its XCD),
+// no sticky error from an earlier launch (sticky_ok).  flag: one int of LDS.
+// No global memory wait comes after the poll, so the caller's loads issue at
+// once.
 __device__ __forceinline__ bool wait_head(unsigned* ctr, unsigned* err, unsigned arrivals,
-                                          bool sticky_ok, int* flag) {
+                                          unsigned offset, bool sticky_ok, int* flag) {
   if (threadIdx.x == 0) {
+    unsigned long long* const c = reinterpret_cast<unsigned long long*>(ctr);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    unsigned v;
+    unsigned long long v;
     bool timeout = false;
-    while (((v = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) &
-            kCountMask) < arrivals) {
+    while (field_sum(v = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) <
+           arrivals) {
       if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
         timeout = true;
         break;
@@ -109,13 +133,14 @@ __device__ __forceinline__ bool wait_head(unsigned* ctr, unsigned* err, unsigned
       __builtin_amdgcn_s_sleep(2);
     }
     if (timeout) __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *flag = !timeout && (v >> kCountBits) == 0 && sticky_ok;
+    *flag = !timeout && ((unsigned)(v >> (8 * offset)) & 0xffu) == arrivals && sticky_ok;
   }
   __syncthreads();
   return *flag != 0;
 }
 
-// Reduce block rb (0-based, rb % 8 its XCD): items of 2048 weight elements,
+// Reduce block rb (0-based; rb % 8 picks the XCD's heads, since rb and the
+// block index agree mod 8): items of 2048 weight elements,
 // the P2 items of each head of this XCD in turn, every per_xcd-th one from
 // rb / 8.  per_xcd <= P2, so each of the XCD's reduce blocks waits once on
 // every head of the XCD.  The two halves of the workgroup take the two
@@ -140,7 +165,7 @@ __device__ __forceinline__ void reduce_blocks(int rb, uint16_t* lds, const float
   float* const tr = reinterpret_cast<float*>(lds) + 1024 * half;  // U x 2 x 1024 floats
   int* const flag = reinterpret_cast<int*>(lds) + 2048 * U;
   unsigned* const err = sync + kSyncWords * heads;
-  const bool here = hw_xcd() == (unsigned)xcd;
+  const unsigned offset = dispatch_offset(blockIdx.x);
   bool sticky_ok = true;
   if (threadIdx.x == 0)
     sticky_ok = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0;
@@ -150,8 +175,9 @@ __device__ __forceinline__ void reduce_blocks(int rb, uint16_t* lds, const float
   auto finish_head = [&](int hl) {
     if (threadIdx.x == 0 && passed == (unsigned)per_xcd - 1) {
       unsigned* ctr = sync + kSyncWords * (xcd + 8 * hl);
-      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctr + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<unsigned long long*>(ctr), 0ull, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctr + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
   for (int i = idx; i < items;) {
@@ -170,12 +196,12 @@ __device__ __forceinline__ void reduce_blocks(int rb, uint16_t* lds, const float
       if (cur >= 0) finish_head(cur);
       cur = hl;
       unsigned* ctr = sync + kSyncWords * hd;
-      ok = wait_head(ctr, err, arrivals, sticky_ok, flag) && here;
+      ok = wait_head(ctr, err, arrivals, offset, sticky_ok, flag);
       if (threadIdx.x == 0) {
         // The lane index (0 here) keeps the address lane-varying to the
         // compiler: a uniform one gets a wave-wide scan around the atomic
         // that waits for its result at once, while only finish_head needs it.
-        unsigned* done = ctr + 1 + __builtin_amdgcn_mbcnt_lo(~0u, 0u);
+        unsigned* done = ctr + 2 + __builtin_amdgcn_mbcnt_lo(~0u, 0u);
         passed = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -226,7 +252,9 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
                              const uint16_t* v, const float* eta, int64_t n_kv, int64_t ld,
                              int heads, int d, int h, WSet w, float* part, UpdatePlan plan,
                              hipStream_t st, const FrameReduce* fr) {
-  if (plan.splits <= 0 || n_kv <= 0 || n_q <= 0) return hipErrorInvalidValue;
+  // n_q = 0 (no read) only with the reduce: an update step in one launch
+  if (plan.splits <= 0 || n_kv <= 0 || n_q < 0 || (n_q == 0 && fr == nullptr))
+    return hipErrorInvalidValue;
   if (plan.tg != 1 && plan.tg != 2) return hipErrorInvalidValue;
   if (fr && (!frame_fuses_reduce(heads, n_kv) || fr->sync == nullptr))
     return hipErrorInvalidValue;
@@ -250,6 +278,7 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
     const int p2 = 3 * h * d / 2048;
     red_per_xcd = p2 < kRedPerXcd ? p2 : kRedPerXcd;
     arrivals = (unsigned)(plan.splits * nsl + ap.splits);
+    if (arrivals > kMaxArrivals) return hipErrorInvalidValue;  // one byte per offset
     ro = fr->out;
     sync = fr->sync;
   }

@@ -119,9 +119,9 @@ __device__ __forceinline__ void gate_backward(float x, float b, float e, float& 
 }
 
 // Block -> (pair, slice) of the update: blocks are dispatched round-robin
-// over the 8 XCDs; the NSL hidden slices of one (head, chunk) pair get ids 8
-// apart, so they run on the same XCD at about the same time and share K/V
-// through its L2.  Pair p is head p % heads of token chunk p / heads; p >=
+// over the 8 XCDs (block b on XCD (b + s) mod 8, s fixed within a launch);
+// the NSL hidden slices of one (head, chunk) pair get ids 8 apart, so they
+// run on the same XCD at about the same time and share K/V through its L2.  Pair p is head p % heads of token chunk p / heads; p >=
 // heads * splits marks a block without work.  With heads a multiple of 8,
 // every block of head j has an id of j's residue mod 8.
 template <int NSL>
@@ -131,8 +131,9 @@ __device__ __forceinline__ int upd_block_pair(int blk) {
 }
 
 // The work of update block `blk` (one workgroup of 512 threads): the kernels
-// that run it pass their block index (offset so that blk % 8 is still the
-// block's XCD) and a 16-byte-aligned LDS buffer of UpdCfg::LDS_ELEMS elements.
+// that run it pass their block index (offset by a multiple of 8, so that
+// blocks whose indices agree mod 8 still share an XCD) and a 16-byte-aligned
+// LDS buffer of UpdCfg::LDS_ELEMS elements.
 // With LOSS, the block also sums u' . e over its tokens and hidden units (u'
 // = -log2(e) u and e = W2^T (eta v) are both in registers for the gate
 // backward) and writes the sum to loss_part[(chunk * heads + head) * NSL +

@@ -273,9 +273,10 @@ struct FrameReduce {
 
 // The apply of n_q queries and the update partial sums over n_kv tokens
 // (plan = plan_update(n_kv, ...)), both through the bf16 set w, in one launch
-// (frame_bf16.hip).  n_q, n_kv > 0; q / o and k / v rows share the stride ld.
+// (frame_bf16.hip).  n_kv > 0; q / o and k / v rows share the stride ld.
 // fr non-null (frame_fuses_reduce must hold): the launch also reduces the
-// partial sums into fr->out, as launch_reduce would.
+// partial sums into fr->out, as launch_reduce would; then n_q may be 0 (a
+// whole update step in one launch), else n_q > 0.
 hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const uint16_t* k,
                              const uint16_t* v, const float* eta, int64_t n_kv, int64_t ld,
                              int heads, int d, int h, WSet w, float* part, UpdatePlan plan,

@@ -3,7 +3,12 @@
 For heads a multiple of 8 and frames of at most 65,536 tokens, the launch that
 reads a frame and computes its partial sums also reduces them: its last
 workgroups wait on per-head arrival counters in the workspace, then run the
-reduce kernel's code.  These tests hold it to the separate kernels bit for bit.
+reduce kernel's code.  An update step without a read (zm_ttt_update,
+update_apply, the update-then-read stream order, inner steps) takes the same
+launch with no read blocks.  These tests hold it to the separate kernels bit
+for bit; the loss variant of the update (zm_ttt_update_loss) is never fused
+and serves as the separate-kernel reference where every other entry point
+fuses.
 The cases cover every narrow shape, 8 to 64 heads, ragged and single-tile
 frames, both update shapes (short frames take two token groups, 65,536 tokens
 take one), and the first frame past the limit, which takes the separate reduce.
@@ -37,6 +42,14 @@ def sync_range(heads, d, h):
     return 2 * set_bytes, 2 * set_bytes + 256 * (heads + 1)
 
 
+def separate_update(k, v, eta, w, renorm=True):
+    """A step through the separate update and reduce kernels: the loss variant
+    of the update is never fused, and its weights equal the plain update's
+    bit for bit (tests/test_virtual_loss_gpu.py)."""
+    w_new, _ = zm.update_loss(k, v, eta, *w, renorm=renorm)
+    return list(w_new)
+
+
 def workspace(w, q, n):
     desc = zm.make_desc(*w, zm.BF16, True, q, q)
     return torch.zeros(zm.workspace_size(desc, n, n), dtype=torch.uint8, device="cuda")
@@ -60,7 +73,7 @@ def test_fused_reduce_equals_separate_kernels(heads, d, h, n):
     o = zm.stream_step(q, k, v, eta, *state, renorm=True, order=zm.APPLY_THEN_UPDATE,
                        workspace=ws)
     o_ref = zm.apply(q, *w)
-    w_ref = zm.update(k, v, eta, *w, renorm=True)
+    w_ref = separate_update(k, v, eta, w)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref)
     for a, b in zip(state, w_ref):
@@ -73,7 +86,7 @@ def test_fused_reduce_equals_separate_kernels(heads, d, h, n):
 def test_emitting_chain_equals_separate_calls(renorm):
     """Frames that keep W's bf16 copies in the workspace (the reduce blocks
     write them while other heads' blocks still read theirs) against a plain
-    loop of zm_ttt_apply / zm_ttt_update."""
+    loop of zm_ttt_apply and separate update kernels."""
     heads, d, h = 8, 128, 256
     sizes = [1374, 1001, 33, 1374, 4096]
     n = sum(sizes)
@@ -88,7 +101,7 @@ def test_emitting_chain_equals_separate_calls(renorm):
         o = zm.stream_step(q[sl], k[sl], v[sl], eta[sl], *state, renorm=renorm, workspace=ws,
                            emit_bf16=True, reuse_bf16=i > 0)
         o_ref = zm.apply(q[sl], *ref)
-        ref = list(zm.update(k[sl], v[sl], eta[sl], *ref, renorm=renorm))
+        ref = separate_update(k[sl], v[sl], eta[sl], ref, renorm=renorm)
         torch.cuda.synchronize()
         assert torch.equal(o, o_ref), i
         for a, b in zip(state, ref):
@@ -119,7 +132,7 @@ def test_sticky_error_word_gives_nan_until_a_cast_clears_it():
     # a call that casts clears the word: fresh weights give the separate result again
     state = [t.clone() for t in w]
     zm.stream_step(q, k, v, eta, *state, renorm=True, workspace=ws)
-    w_ref = zm.update(k, v, eta, *w, renorm=True)
+    w_ref = separate_update(k, v, eta, w)
     torch.cuda.synchronize()
     for x, y in zip(state, w_ref):
         assert torch.equal(x, y)
@@ -143,8 +156,104 @@ def test_chunked_block_causal_fuses_every_step():
         if s == e:
             continue
         o_ref[s:e] = zm.apply(q[s:e], *ref)
-        ref = list(zm.update(k[s:e], v[s:e], eta[s:e], *ref, renorm=True))
+        ref = separate_update(k[s:e], v[s:e], eta[s:e], ref)
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref)
     for a, b in zip(state, ref):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("heads,d,h,n", [
+    (8, 128, 256, 1374), (8, 128, 256, 33), (16, 64, 128, 777), (64, 128, 256, 2000),
+    (8, 64, 256, FUSE_MAX), (8, 128, 128, 10_992),
+])
+def test_update_alone_fuses_and_equals_separate_kernels(heads, d, h, n):
+    """zm_ttt_update and zm_ttt_update_apply on short chunks run the update
+    and its reduce as one launch (no read blocks)."""
+    say(f"case fused update alone H={heads} d={d} h={h} n={n}")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=83 + heads + n % 11)
+    ref = separate_update(k, v, eta, w)
+    got = zm.update(k, v, eta, *w, renorm=True)
+    (w_ua, o_ua) = zm.update_apply(k, v, eta, q, *w, renorm=True)
+    o_ref = zm.apply(q, *ref)
+    torch.cuda.synchronize()
+    for a, b, c in zip(got, w_ua, ref):
+        assert torch.equal(a, c)
+        assert torch.equal(b, c)
+    assert torch.equal(o_ua, o_ref)
+
+
+def test_update_then_read_stream_equals_separate_kernels():
+    """Frames in the update-then-read order with the bf16 flags: each frame's
+    update and reduce share a launch, whose reduce also writes the bf16 copies
+    the read uses."""
+    heads, d, h = 8, 128, 256
+    sizes = [1374, 700, 33, 1374]
+    say("case fused update-then-read stream")
+    q, k, v, eta, w = tensors(sum(sizes), heads, d, h, seed=85)
+    state = [t.clone() for t in w]
+    ref = [t.clone() for t in w]
+    ws = workspace(w, q, max(sizes))
+    s = 0
+    for i, m in enumerate(sizes):
+        sl = slice(s, s + m)
+        o = zm.stream_step(q[sl], k[sl], v[sl], eta[sl], *state, renorm=True,
+                           order=zm.UPDATE_THEN_APPLY, workspace=ws, emit_bf16=True,
+                           reuse_bf16=i > 0)
+        ref = separate_update(k[sl], v[sl], eta[sl], ref)
+        o_ref = zm.apply(q[sl], *ref)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), i
+        for a, b in zip(state, ref):
+            assert torch.equal(a, b), i
+        s += m
+    a, b = sync_range(heads, d, h)
+    assert int(ws[a:b].count_nonzero()) == 0
+
+
+def test_chunked_inner_steps_fuse_every_step():
+    """Two inner steps per chunk: the first shares the read's launch, the
+    second runs as an update-and-reduce launch of its own."""
+    heads, d, h = 8, 128, 256
+    offsets = [0, 1374, 2074, 2107]
+    say("case fused chunked inner steps")
+    q, k, v, eta, w = tensors(offsets[-1], heads, d, h, seed=87)
+    state = [t.clone() for t in w]
+    o = zm.chunked(q, k, v, eta, offsets, *state, renorm=True, order=zm.APPLY_THEN_UPDATE,
+                   inner_steps=2)
+    ref = [t.clone() for t in w]
+    o_ref = torch.zeros_like(o)
+    for c in range(len(offsets) - 1):
+        s, e = offsets[c], offsets[c + 1]
+        o_ref[s:e] = zm.apply(q[s:e], *ref)
+        for _ in range(2):
+            ref = separate_update(k[s:e], v[s:e], eta[s:e], ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    for a, b in zip(state, ref):
+        assert torch.equal(a, b)
+
+
+def test_any_dispatch_offset_gives_the_separate_result():
+    """Blocks go to XCD (block + s) mod 8 with an offset s that follows from
+    the launches before; a small torch kernel of a varying grid before each
+    call moves it.  Every offset must give the separate kernels' result (the
+    reduce checks that a head's blocks share an XCD, not which one)."""
+    heads, d, h, n = 8, 128, 256, 1374
+    say("case fused reduce under varying dispatch offsets")
+    q, k, v, eta, w = tensors(n, heads, d, h, seed=89)
+    ref = separate_update(k, v, eta, w)
+    o_ref = zm.apply(q, *w)
+    ws = workspace(w, q, n)
+    pad = torch.ones(64 * 1024 * 8, device="cuda")
+    for m in range(1, 9):   # elementwise kernels of different grids
+        pad[: m * 256 * 4 + 17].mul_(1.0)
+        state = [t.clone() for t in w]
+        o = zm.stream_step(q, k, v, eta, *state, renorm=True, workspace=ws)
+        pad[: m * 512 + 3].add_(0.0)
+        got = zm.update(k, v, eta, *w, renorm=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), m
+        for a, b, c in zip(state, got, ref):
+            assert torch.equal(a, c), m
+            assert torch.equal(b, c), m
