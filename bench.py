@@ -176,6 +176,30 @@ def time_region(torch, stream, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
+# Chunks of at most this many tokens, with heads a multiple of 8 and the
+# gradient rule, have their partial sums reduced inside the update's own
+# launch (the library's frame_fuses_reduce): the update stage's events then
+# cover the update and its reduce.
+FUSE_MAX_TOKENS = 65536
+
+
+def update_fuses_reduce(wl, rule_gradient=True):
+    return (wl.io_dtype == "bf16" and wl.d_head in (64, 128) and wl.heads % 8 == 0
+            and rule_gradient and 0 < wl.tokens_per_frame <= FUSE_MAX_TOKENS
+            if wl.streaming else
+            wl.io_dtype == "bf16" and wl.d_head in (64, 128) and wl.heads % 8 == 0
+            and rule_gradient and 0 < wl.n_kv <= FUSE_MAX_TOKENS)
+
+
+def update_token_groups(n, heads, d_hidden):
+    """The update's workgroup shape for n tokens (the library's plan_update):
+    2 token groups when chunks of 4 32-token tiles would leave compute units
+    idle, else 1."""
+    nsl = max(d_hidden // 128, 1)
+    target = max(256 // (heads * nsl), 1)
+    return 2 if -(-(-(-n // 32)) // 4) < target and d_hidden >= 128 else 1
+
+
 def stage_ms(torch, zm, fn, steps=5):
     """Average ms of the update partial sums (stage 1) and the apply (stage 3)
     over `steps` calls of fn, from the library's events around each stage."""
@@ -302,6 +326,8 @@ def run_configs(dev, torch, zm, WL, f700_inputs, seed):
                         "frac_bf16_peak": round(flops / (per_layer / 1e3) / 1e12
                                                 / PEAK_BF16_TFLOPS, 4),
                         "kernels_ms": stage_ms(torch, zm, lambda: one(0))})
+            if update_fuses_reduce(wl):
+                rec["kernels_ms"]["update_includes_reduce"] = True
             if name == "f100":
                 rec["target_view_queries"] = wl.extra_queries
             del wsets, w_out
@@ -580,6 +606,11 @@ def main():
             kname = ("update stage (hipBLASLt E and reduction GEMMs + k_wide_rows update)"
                      if dom == "update" else
                      "apply stage (k_wide_rows read + hipBLASLt output GEMM)")
+        elif update_fuses_reduce(wl, rule == zm.STEP_GRADIENT):
+            tg = update_token_groups(wl.n_kv, wl.heads, wl.d_hidden)
+            kname = (f"k_frame_bf16<128,256,{tg}> (update and its reduce in one launch)"
+                     if dom == "update" else "k_apply_bf16<128,256>")
+            kern["reduce"]["in_update_launch"] = True
         else:
             kname = "k_update_bf16<128,256,1>" if dom == "update" else "k_apply_bf16<128,256>"
         result["roofline"] = {

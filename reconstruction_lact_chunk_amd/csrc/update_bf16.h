@@ -121,13 +121,14 @@ __device__ __forceinline__ void gate_backward(float x, float b, float e, float& 
 // Block -> (pair, slice) of the update: blocks are dispatched round-robin
 // over the 8 XCDs (block b on XCD (b + s) mod 8, s fixed within a launch);
 // the NSL hidden slices of one (head, chunk) pair get ids 8 apart, so they
-// run on the same XCD at about the same time and share K/V through its L2.  Pair p is head p % heads of token chunk p / heads; p >=
-// heads * splits marks a block without work.  With heads a multiple of 8,
-// every block of head j has an id of j's residue mod 8.
+// run on the same XCD at about the same time and share K/V through its L2.
+// Pair p is head p % heads of token chunk p / heads; p >= heads * splits
+// marks a block without work.  With heads a multiple of 8, every block of
+// head j has an id of j's residue mod 8.
 template <int NSL>
 __device__ __forceinline__ int upd_block_pair(int blk) {
-  const int xcd = blk & 7, r = blk >> 3;
-  return (r / NSL) * 8 + xcd;
+  const int lane8 = blk & 7, r = blk >> 3;
+  return (r / NSL) * 8 + lane8;
 }
 
 // The work of update block `blk` (one workgroup of 512 threads): the kernels

@@ -64,3 +64,19 @@ def test_cpu_baseline_record(step_rule):
     assert rec["kind"] == "oracle" and rec["unit"] == "tokens/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     assert str(n) in rec["sample"] and bench.blas_name() in rec["sample"]
+
+
+def test_bench_mirrors_the_update_plan_and_the_fused_reduce_rule():
+    """bench.py names the update's kernel from its own copies of the planner's
+    token-group rule and of the rule that reduces short chunks inside the
+    update's launch; both must agree with the host model of the library."""
+    import itertools
+    import test_tiling_host as TH
+    import workloads as WL
+    for n, heads, h in itertools.product([1, 33, 1374, 5000, 10_992, 65_536, 137_400],
+                                         [8, 16, 64], [128, 256]):
+        assert bench.update_token_groups(n, heads, h) == TH.plan_update_tg(n, heads, h)[2]
+    fused = {name: bench.update_fuses_reduce(wl) for name, wl in WL.WORKLOADS.items()}
+    assert fused["f8"] and fused["stream256"] and fused["chunked256"]
+    assert not fused["f700"] and not fused["f100"] and not fused["tiny"]
+    assert not bench.update_fuses_reduce(WL.WORKLOADS["f8"], rule_gradient=False)
