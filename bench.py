@@ -176,19 +176,14 @@ def time_region(torch, stream, fn, steps, warmup):
     return a.elapsed_time(b) / steps
 
 
-# Chunks of at most this many tokens, with heads a multiple of 8 and the
-# gradient rule, have their partial sums reduced inside the update's own
-# launch (the library's frame_fuses_reduce): the update stage's events then
-# cover the update and its reduce.
-FUSE_MAX_TOKENS = 65536
-
-
 def update_fuses_reduce(wl, rule_gradient=True):
+    """Whether the library reduces the update's partial sums inside the
+    update's own launch (its frame_fuses_reduce): heads a multiple of 8, the
+    gradient rule, and chunks short enough for the two-token-group update.
+    The update stage's events then cover the update and its reduce."""
+    n = wl.tokens_per_frame if wl.streaming else wl.n_kv
     return (wl.io_dtype == "bf16" and wl.d_head in (64, 128) and wl.heads % 8 == 0
-            and rule_gradient and 0 < wl.tokens_per_frame <= FUSE_MAX_TOKENS
-            if wl.streaming else
-            wl.io_dtype == "bf16" and wl.d_head in (64, 128) and wl.heads % 8 == 0
-            and rule_gradient and 0 < wl.n_kv <= FUSE_MAX_TOKENS)
+            and rule_gradient and n > 0 and update_token_groups(n, wl.heads, wl.d_hidden) == 2)
 
 
 def update_token_groups(n, heads, d_hidden):

@@ -12,12 +12,12 @@
 // kernel; the apply blocks follow.  Results are those of the two separate
 // kernels, bit for bit: each block runs the same code on the same tokens.
 //
-// For short chunks the launch can also reduce the partial sums (the step and
-// renorm of the review of ZipMap, Method 2, after Eq. (3)).  Reduce blocks
-// come last.  Each waits until every update and apply block of its head has
-// finished, then runs the reduce kernel's per-element code
-// (reduce_rows.h) on its share of the head.  Results again equal the separate
-// kernels bit for bit.  This removes the reduce's launch and the wait between
+// For short chunks (those that take the two-token-group update) the launch
+// can also reduce the partial sums (the step and renorm of the review of
+// ZipMap, Method 2, after Eq. (3)).  Reduce blocks come last.  Each waits
+// until every update and apply block of its head has finished, then runs the
+// reduce kernel's per-element code (reduce_rows.h) on its share of the head.
+// Results again equal the separate kernels bit for bit.  This removes the reduce's launch and the wait between
 // the two launches; the partial sums are written and read back within one
 // XCD, where most of the reads hit its L2.
 //
@@ -51,9 +51,10 @@
 // later than the reduce block itself and finishes on its own; the reduce
 // blocks also stay fewer than the compute units of an XCD.  The poll is
 // bounded in time all the same (kSpinTicks of the 100 MHz real-time clock,
-// far beyond the longest frame the planner fuses): a reduce block that runs
-// out sets a sticky error word and writes NaN, and so does every later fused
-// launch on this workspace until a cast clears the word.
+// far beyond the longest chunk that takes this launch, a few thousand tokens):
+// a reduce block that runs out sets a sticky error word and writes NaN, and
+// so does every later fused launch on this workspace until a cast clears the
+// word.
 //
 // Each reduce block counts itself past the wait in another word of its
 // head; the last one to count clears the counter and that word once its own
@@ -256,7 +257,7 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
   if (plan.splits <= 0 || n_kv <= 0 || n_q < 0 || (n_q == 0 && fr == nullptr))
     return hipErrorInvalidValue;
   if (plan.tg != 1 && plan.tg != 2) return hipErrorInvalidValue;
-  if (fr && (!frame_fuses_reduce(heads, n_kv) || fr->sync == nullptr))
+  if (fr && (!frame_fuses_reduce(heads, plan) || fr->sync == nullptr))
     return hipErrorInvalidValue;
   const int nsl = plan_slices(plan, h);
   const int64_t pairs = (int64_t)heads * plan.splits;

@@ -255,16 +255,19 @@ hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t 
 // The reduce inside the shared read-and-update launch (frame_bf16.hip): the
 // launch's last workgroups wait for the update and read workgroups of their
 // head, then reduce its partial sums, which are still in that XCD's L2.  It
-// needs every workgroup of a head on one XCD (heads a multiple of 8) and a
-// wait that ends well within its bound (frames of at most kFuseMaxTokens).
-// The sync region holds kSyncWords words per head and one more block for a
-// sticky error word; it must be zero before the first such launch (launch_cast
-// clears it) and each launch leaves it zero.
+// needs every workgroup of a head on one XCD (heads a multiple of 8), and it
+// pays only where the partial sums are few: chunks short enough for the
+// two-token-group update (plan.tg == 2), whose partial sums are halved and
+// mostly stay in the L2.  For longer chunks (16 slots of 3.1 MB per 8 heads of
+// 128 / 256) the reduce reads them from memory either way, and in one launch it
+// ran no faster than as a launch of its own.  The sync region holds
+// kSyncWords words per head and one more block for a sticky error word; it
+// must be zero before the first such launch (launch_cast clears it) and each
+// launch leaves it zero.
 constexpr int kSyncWords = 64;                  // 256 bytes: one head's counters
-constexpr int64_t kFuseMaxTokens = 65536;
 inline size_t frame_sync_words(int heads) { return (size_t)kSyncWords * (heads + 1); }
-inline bool frame_fuses_reduce(int heads, int64_t n_kv) {
-  return heads % 8 == 0 && n_kv > 0 && n_kv <= kFuseMaxTokens;
+inline bool frame_fuses_reduce(int heads, const UpdatePlan& plan) {
+  return heads % 8 == 0 && plan.tg == 2 && plan.splits > 0;
 }
 struct FrameReduce {
   unsigned* sync;   // frame_sync_words(heads) words

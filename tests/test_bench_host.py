@@ -77,6 +77,6 @@ def test_bench_mirrors_the_update_plan_and_the_fused_reduce_rule():
                                          [8, 16, 64], [128, 256]):
         assert bench.update_token_groups(n, heads, h) == TH.plan_update_tg(n, heads, h)[2]
     fused = {name: bench.update_fuses_reduce(wl) for name, wl in WL.WORKLOADS.items()}
-    assert fused["f8"] and fused["stream256"] and fused["chunked256"]
-    assert not fused["f700"] and not fused["f100"] and not fused["tiny"]
-    assert not bench.update_fuses_reduce(WL.WORKLOADS["f8"], rule_gradient=False)
+    assert fused["stream256"] and fused["chunked256"]
+    assert not fused["f700"] and not fused["f100"] and not fused["f8"] and not fused["tiny"]
+    assert not bench.update_fuses_reduce(WL.WORKLOADS["stream256"], rule_gradient=False)

@@ -1,7 +1,8 @@
 """The reduce inside the shared read-and-update launch (frame_bf16.hip).
 
-For heads a multiple of 8 and frames of at most 65,536 tokens, the launch that
-reads a frame and computes its partial sums also reduces them: its last
+For heads a multiple of 8 and chunks short enough for the two-token-group
+update, the launch that reads a frame and computes its partial sums also
+reduces them: its last
 workgroups wait on per-head arrival counters in the workspace, then run the
 reduce kernel's code.  An update step without a read (zm_ttt_update,
 update_apply, the update-then-read stream order, inner steps) takes the same
@@ -10,8 +11,8 @@ for bit; the loss variant of the update (zm_ttt_update_loss) is never fused
 and serves as the separate-kernel reference where every other entry point
 fuses.
 The cases cover every narrow shape, 8 to 64 heads, ragged and single-tile
-frames, both update shapes (short frames take two token groups, 65,536 tokens
-take one), and the first frame past the limit, which takes the separate reduce.
+frames, the longest chunk that takes two token groups, and the first that
+takes one, which keeps the separate reduce.
 The counters must be zero after every launch.  A sticky error word set from
 the host must turn the stepped weights into NaN rather than plausible values.
 """
@@ -19,12 +20,25 @@ import pytest
 import torch
 
 import reconstruction_lact_chunk_amd as zm
+import test_tiling_host as TH
 import workloads as WL
 from test_parity_gpu import say
 
 pytestmark = pytest.mark.gpu
 
-FUSE_MAX = 65536
+
+def last_fused(heads, h):
+    """The longest chunk whose update takes two token groups (and so the
+    in-launch reduce); one token more takes one group and the separate reduce."""
+    n = 32
+    while TH.plan_update_tg(n + 32, heads, h)[2] == 2:
+        n += 32
+    while TH.plan_update_tg(n + 1, heads, h)[2] == 2:
+        n += 1
+    return n
+
+
+N8 = last_fused(8, 256)
 
 
 def tensors(n, heads, d, h, seed):
@@ -62,8 +76,8 @@ def workspace(w, q, n):
     (8, 64, 128, 500),         # 12 reduce blocks per XCD (a head's items)
     (24, 64, 256, 4000),       # three heads per XCD
     (64, 64, 128, 1374),       # eight heads per XCD
-    (8, 128, 256, FUSE_MAX),   # the longest fused frame (one token group)
-    (8, 128, 256, FUSE_MAX + 1),   # separate reduce
+    (8, 128, 256, N8),         # the longest fused chunk
+    (8, 128, 256, N8 + 1),     # one group: separate reduce
 ])
 def test_fused_reduce_equals_separate_kernels(heads, d, h, n):
     say(f"case fused reduce H={heads} d={d} h={h} n={n}")
@@ -164,8 +178,8 @@ def test_chunked_block_causal_fuses_every_step():
 
 
 @pytest.mark.parametrize("heads,d,h,n", [
-    (8, 128, 256, 1374), (8, 128, 256, 33), (16, 64, 128, 777), (64, 128, 256, 2000),
-    (8, 64, 256, FUSE_MAX), (8, 128, 128, 10_992),
+    (8, 128, 256, 1374), (8, 128, 256, 33), (16, 64, 128, 777), (64, 128, 256, 200),
+    (8, 64, 256, N8), (8, 128, 128, last_fused(8, 128)), (8, 128, 256, 10_992),
 ])
 def test_update_alone_fuses_and_equals_separate_kernels(heads, d, h, n):
     """zm_ttt_update and zm_ttt_update_apply on short chunks run the update

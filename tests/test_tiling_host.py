@@ -695,7 +695,6 @@ def test_reserved_slots_cover_every_shorter_update(heads, d_hidden):
 
 # ---- the reduce inside the shared read-and-update launch (frame_bf16.hip) ----
 
-FUSE_MAX = 65536
 RED_PER_XCD = 24
 
 
@@ -755,9 +754,12 @@ def frame_blocks(n, heads, d, h):
 @pytest.mark.parametrize("heads,d,h", [(8, 128, 256), (8, 128, 128), (8, 64, 256), (8, 64, 128),
                                        (16, 128, 256), (24, 64, 256), (64, 64, 128),
                                        (64, 128, 256)])
-@pytest.mark.parametrize("n", [1, 33, 500, 1374, 4000, 20_000, FUSE_MAX])
+@pytest.mark.parametrize("n", [1, 33, 500, 1374, 1800, 4000])
 def test_fused_reduce_blocks(heads, d, h, n):
+    if plan_update_tg(n, heads, h)[2] != 2:
+        pytest.skip("one token group: no in-launch reduce")
     signal, reduce, arrivals, per_xcd = frame_blocks(n, heads, d, h)
+    assert arrivals <= 255                            # one byte per dispatch offset
     assert per_xcd < 32                                # fewer than an XCD's compute units
     # every signalling block runs on its head's XCD and each head counts
     # exactly the arrivals its reduce blocks wait for
