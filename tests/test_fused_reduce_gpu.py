@@ -271,3 +271,59 @@ def test_any_dispatch_offset_gives_the_separate_result():
         for a, b, c in zip(state, got, ref):
             assert torch.equal(a, c), m
             assert torch.equal(b, c), m
+
+
+def test_graph_replays_of_fused_launches_equal_eager():
+    """Stream frames and an update_apply short enough to reduce inside the
+    update's launch, captured in a HIP graph and replayed several times with
+    eager work of varying grids in between (which moves the dispatch offset):
+    every replay must equal the eager result bitwise.  The graph holds no
+    memset: the cast clears the sync words with a kernel."""
+    heads, d, h, n = 8, 128, 256, 1374
+    say("case fused reduce under HIP graph replay")
+    q, k, v, eta, w = tensors(2 * n, heads, d, h, seed=91)
+    ws = workspace(w, q, 2 * n)
+    state = [t.clone() for t in w]
+    w_out = [torch.empty_like(t) for t in w]
+    o1, o2, o3 = (torch.empty_like(q[:n]) for _ in range(3))
+
+    def call():
+        for t, t0 in zip(state, w):
+            t.copy_(t0)
+        zm.stream_step(q[:n], k[:n], v[:n], eta[:n], *state, renorm=True, out=o1, workspace=ws,
+                       emit_bf16=True)
+        zm.stream_step(q[n:], k[n:], v[n:], eta[n:], *state, renorm=True, out=o2, workspace=ws,
+                       emit_bf16=True, reuse_bf16=True)
+        zm.update_apply(k[:n], v[:n], eta[:n], q[:n], *w, renorm=True, w_out=w_out, out=o3,
+                        workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in state + w_out + [o1, o2, o3]]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    pad = torch.ones(1 << 20, device="cuda")
+    for r in range(4):
+        for t in state + w_out + [o1, o2, o3]:
+            t.zero_()
+        pad[: 1000 * r + 77].mul_(1.0)   # eager work of a varying grid
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(state + w_out + [o1, o2, o3], ref):
+            assert torch.equal(a, b), r
+    # and the eager result is the separate kernels' one
+    w1 = separate_update(k[:n], v[:n], eta[:n], w)
+    w2 = separate_update(k[n:], v[n:], eta[n:], w1)
+    torch.cuda.synchronize()
+    for a, b in zip(ref[:3], w2):
+        assert torch.equal(a, b)
+    for a, b in zip(ref[3:6], w1):
+        assert torch.equal(a, b)
