@@ -127,7 +127,9 @@ __device__ __forceinline__ void apply_tiles(
   const int lane_off = has_item ? s_tok * (int)ld + head * D + 8 * s_ch : head * D;
   auto fetch = [&](int it) {
     const int64_t t0 = t_begin + (int64_t)it * T;
-    if (t0 + T <= t_end) return *(const u32x4*)(qp + t0 * ld + lane_off);
+    // queries are read once and outputs written once: non-temporal, so the L2
+    // keeps the weights (and, in the shared launch, the partial sums) instead
+    if (t0 + T <= t_end) return __builtin_nontemporal_load((const u32x4*)(qp + t0 * ld + lane_off));
     const int64_t tc = (has_item && t0 < t_end && t0 + s_tok < t_end) ? t0 + s_tok
                        : (t0 < t_end ? t0 : t_begin);
     return *(const u32x4*)(qp + tc * ld + head * D + (has_item ? 8 * s_ch : 0));
@@ -231,7 +233,7 @@ __device__ __forceinline__ void apply_tiles(
       if (!has_item) return;
     }
     const int64_t tile0 = t_begin + (int64_t)it * T;
-    if (tile0 + s_tok < t_end) *(u32x4*)(op + tile0 * ld + o_lane_off) = v;
+    if (tile0 + s_tok < t_end) __builtin_nontemporal_store(v, (u32x4*)(op + tile0 * ld + o_lane_off));
   };
   auto o_from_lds = [&](int it) { o_store(it, o_read(it)); };
   // SiLU gate of element e (= (mb * NB + nb) * 4 + i) into the packed U rows

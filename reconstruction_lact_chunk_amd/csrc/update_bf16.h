@@ -218,8 +218,11 @@ __device__ __forceinline__ void update_tiles(
 #pragma unroll
       for (int q = 0; q < IPT; ++q) {
         const int64_t tq = t0 + (int64_t)q * QROWS;
-        r.k[q] = *(const u32x4*)(kp + tq * ld + lane_tok_off[0]);
-        r.v[q] = *(const u32x4*)(vp + tq * ld + lane_tok_off[0]);
+        // Tokens are streamed (read by the NSL slices of one XCD, then dead):
+        // non-temporal loads let the L2 evict them first, which keeps more of
+        // a short chunk's partial sums there for the in-launch reduce.
+        r.k[q] = __builtin_nontemporal_load((const u32x4*)(kp + tq * ld + lane_tok_off[0]));
+        r.v[q] = __builtin_nontemporal_load((const u32x4*)(vp + tq * ld + lane_tok_off[0]));
         r.e[q] = eta[tq * heads + lane_eta_off[0]];
       }
     } else if (TG == 2 && t0 >= t_end) {
