@@ -37,7 +37,12 @@
  *    round them to bf16 operands and accumulate in fp32.
  *  - Workspace: device scratch of at least zm_ttt_workspace_size() bytes,
  *    256-byte aligned.  Calls sharing one workspace must not overlap in time;
- *    calls on distinct workspaces and streams are independent.
+ *    calls on distinct workspaces and streams are independent.  For short
+ *    chunks (bf16 io, heads a multiple of 8, the gradient step) an update
+ *    reduces its partial sums inside its own launch, whose workgroups meet
+ *    at counters kept in the workspace; should that ever fail (a wait past
+ *    its 2 s bound), the stepped weights come out NaN, never plausible wrong
+ *    values.
  *  - stream: a hipStream_t passed as void*; NULL is the default stream.
  *    Every entry point only enqueues work and returns.
  *  - Errors: arguments are checked on the host before any HIP call; a failed
@@ -311,7 +316,8 @@ ZM_API int zm_ttt_version(void);
  * events[2s] before and events[2s+1] after itself on the launch stream, for
  * each non-NULL slot.  Where a chunk's read and its update's partial sums
  * share one launch (bf16 APPLY_THEN_UPDATE), the events of stages 1 and 3
- * both bracket that launch.  The events are hipEvent_t handles passed as void*;
+ * both bracket that launch; where the reduce runs inside the update's launch
+ * (short chunks, see Workspace above), so do those of stage 2.  The events are hipEvent_t handles passed as void*;
  * n_events must be 8 (stages 0-3), 10 (0-4) or 14 (0-6) (or 0 with
  * events == NULL to switch off).  Process-wide setting; not for concurrent use
  * from several threads. */

@@ -77,7 +77,9 @@ namespace {
 // Arrival counter of a head: the first 64 bits of its kSyncWords block, 8
 // bits per dispatch offset; word 2 counts the reduce blocks past the wait.
 constexpr unsigned kMaxArrivals = 255;
-constexpr uint64_t kSpinTicks = 50000000;    // 0.5 s of the 100 MHz real-time clock
+// 2 s of the 100 MHz real-time clock: a legitimate wait lasts microseconds,
+// and the bound also covers time the process spends switched off the GPU.
+constexpr uint64_t kSpinTicks = 200000000;
 constexpr int kRedPerXcd = 24;               // at most this many reduce blocks per XCD
 constexpr int kRedU = 2;                     // items a reduce block loads at once
 
