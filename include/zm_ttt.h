@@ -210,9 +210,11 @@ ZM_API int zm_ttt_update_apply(const zm_ttt_desc* desc, int64_t n_kv,
  * device's scratch address.  Results are bitwise those of
  * zm_ttt_update_apply.  Narrow heads only: a call whose workspace need
  * (zm_ttt_workspace_size(desc, n_kv, n_q)) exceeds the scratch returns
- * ZM_ERR_WORKSPACE, and the full-width shape ZM_ERR_UNSUPPORTED.  Nothing in
- * the scratch needs clearing (every kernel writes what the next one reads),
- * and a call leaves its last contents there.  All calls on one GPU share its
+ * ZM_ERR_WORKSPACE, and the full-width shape ZM_ERR_UNSUPPORTED.  Every
+ * kernel writes what the next one reads, except the counters of the
+ * in-launch reduce (see Workspace above), which must start at zero: the
+ * call's first kernel clears them (a kernel, not a memset, so the call can
+ * be captured).  A call leaves its last contents there.  All calls on one GPU share its
  * scratch: calls that overlap in time on one GPU (two streams, two threads)
  * race and give undefined results; order them on one stream. */
 ZM_API int zm_ttt_update_apply_scratch(const zm_ttt_desc* desc, int64_t n_kv,
