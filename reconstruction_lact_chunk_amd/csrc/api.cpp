@@ -270,7 +270,7 @@ int run_update(const zm_ttt_desc* d, int64_t n, const void* k, const void* v, co
                            (int)frame_sync_words(d->heads)));
       }
       Scoped s(kStageUpdate, st);
-      if (!loss && d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, L.plan)) {
+      if (!loss && d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, L.plan, 0)) {
         // short chunk: partial sums and reduce in one launch
         Scoped r(kStageReduce, st);
         const FrameReduce fr{sync, ReduceOut{w1, w2, w3, o1, o2, o3,
@@ -372,7 +372,7 @@ int run_chunk(const zm_ttt_desc* d, int order, bool do_update, int inner, int64_
       float* part = (float*)((char*)ws.p + L.part);
       ZM_TRY(check_part_range(L.part, L.plan.splits, welems, ws.bytes));
       const WSet* out = (emit && updates == 1) ? &a : nullptr;
-      const bool fuse = d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, L.plan);
+      const bool fuse = d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(d->heads, L.plan, n);
       const FrameReduce fr{sync, ReduceOut{w1, w2, w3, w1, w2, w3,
                                            out ? *out : WSet{nullptr, nullptr, nullptr, nullptr},
                                            d->renorm, out ? 1 : 0}};
@@ -438,8 +438,10 @@ int run_chunked_bf16(const zm_ttt_desc* d, int order, int64_t n_chunks, const in
     const UpdatePlan plan = plan_update(len(c), hd, hh);
     ZM_TRY(check_part_range(L0.part, plan.splits, (size_t)hd * hh * dh, ws.bytes));
     const float* e = eta + offsets[c] * hd;
-    const bool fusable = d->step_rule == ZM_STEP_GRADIENT && frame_fuses_reduce(hd, plan);
-    const bool fuse = rc >= 0 && fusable, fuse_alone = rc < 0 && fusable;
+    const bool fuse = rc >= 0 && d->step_rule == ZM_STEP_GRADIENT &&
+                      frame_fuses_reduce(hd, plan, len(rc));
+    const bool fuse_alone = rc < 0 && d->step_rule == ZM_STEP_GRADIENT &&
+                            frame_fuses_reduce(hd, plan, 0);
     {
       Scoped su(kStageUpdate, st);
       if (rc >= 0) {

@@ -259,7 +259,7 @@ hipError_t launch_frame_bf16(const uint16_t* q, uint16_t* o, int64_t n_q, const 
   if (plan.splits <= 0 || n_kv <= 0 || n_q < 0 || (n_q == 0 && fr == nullptr))
     return hipErrorInvalidValue;
   if (plan.tg != 1 && plan.tg != 2) return hipErrorInvalidValue;
-  if (fr && (!frame_fuses_reduce(heads, plan) || fr->sync == nullptr))
+  if (fr && (!frame_fuses_reduce(heads, plan, n_q) || fr->sync == nullptr))
     return hipErrorInvalidValue;
   const int nsl = plan_slices(plan, h);
   const int64_t pairs = (int64_t)heads * plan.splits;

@@ -265,9 +265,14 @@ hipError_t launch_apply_bf16(const uint16_t* q, uint16_t* o, int64_t n, int64_t 
 // must be zero before the first such launch (launch_cast clears it) and each
 // launch leaves it zero.
 constexpr int kSyncWords = 64;                  // 256 bytes: one head's counters
+// Longest read that may share a launch with an in-launch reduce: its blocks
+// must finish well within the reduce blocks' 2 s wait bound (a million
+// queries take about 1.5 ms at 8 heads, 12 ms at 64).
+constexpr int64_t kFuseMaxRead = (int64_t)1 << 20;
 inline size_t frame_sync_words(int heads) { return (size_t)kSyncWords * (heads + 1); }
-inline bool frame_fuses_reduce(int heads, const UpdatePlan& plan) {
-  return heads % 8 == 0 && plan.tg == 2 && plan.splits > 0;
+// n_q: the queries read in the same launch (0 for an update alone).
+inline bool frame_fuses_reduce(int heads, const UpdatePlan& plan, int64_t n_q) {
+  return heads % 8 == 0 && plan.tg == 2 && plan.splits > 0 && n_q >= 0 && n_q <= kFuseMaxRead;
 }
 struct FrameReduce {
   unsigned* sync;   // frame_sync_words(heads) words

@@ -327,3 +327,27 @@ def test_graph_replays_of_fused_launches_equal_eager():
         assert torch.equal(a, b)
     for a, b in zip(ref[3:6], w1):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("n_read", [1 << 20, (1 << 20) + 1])
+def test_long_paired_read_keeps_the_wait_short(n_read):
+    """In the block-causal order chunk c's read shares a launch with chunk
+    c + 1's update.  A short update chunk reduces inside that launch only when
+    the read is at most 2^20 queries, so the reduce blocks never wait on a
+    read long enough to approach their time bound; past it the separate
+    reduce runs.  Both sides of the limit equal the separate kernels."""
+    heads, d, h, short = 8, 64, 128, 1374
+    say(f"case fused reduce beside a long read n_read={n_read}")
+    offsets = [0, n_read, n_read + short]
+    q, k, v, eta, w = tensors(offsets[-1], heads, d, h, seed=93)
+    state = [t.clone() for t in w]
+    o = zm.chunked(q, k, v, eta, offsets, *state, renorm=True, order=zm.UPDATE_THEN_APPLY)
+    ref = separate_update(k[:n_read], v[:n_read], eta[:n_read], w)
+    o_ref0 = zm.apply(q[:n_read], *ref)
+    ref = separate_update(k[n_read:], v[n_read:], eta[n_read:], ref)
+    o_ref1 = zm.apply(q[n_read:], *ref)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:n_read], o_ref0)
+    assert torch.equal(o[n_read:], o_ref1)
+    for a, b in zip(state, ref):
+        assert torch.equal(a, b)
