@@ -786,3 +786,100 @@ def test_fused_reduce_blocks(heads, d, h, n):
             waiters[hd] += 1
     assert (seen == 1).all()
     assert waiters == [per_xcd] * heads
+
+
+# ---- the in-launch reduce's counter protocol (frame_bf16.hip), as a model ----
+
+class SyncModel:
+    """One head's sync words: a 64-bit arrival counter with one 8-bit field
+    per dispatch offset, the count of reduce blocks past their wait, and the
+    sticky error word (shared by the heads; kept here per model)."""
+
+    def __init__(self):
+        self.ctr = 0
+        self.done = 0
+        self.err = 0
+
+
+def run_launch(sync, arrivals, per_head, rng, offsets=None, err_from_host=False):
+    """One launch of one head with a random interleaving of its blocks' steps:
+    `arrivals` signalling blocks (offset per block from `offsets`, default 0)
+    and `per_head` reduce blocks (offset 0).  A reduce block polls, reads the
+    field of its own offset, counts itself past the wait (fetch-add), does
+    its items, and if it counted last clears both words.  Returns the list of
+    (arrivals seen when passing, trusted) per reduce block."""
+    offsets = offsets or [0] * arrivals
+    if err_from_host:
+        sync.err = 1
+    # actor programs as generators yielding after every shared-memory step
+    seen = []
+
+    def arriver(off):
+        sync.ctr += 1 << (8 * off)          # atomic fetch-add
+        yield
+
+    def reducer():
+        polls, timeout = 0, False
+        while True:                        # poll, bounded like the kernel's wait
+            v = sync.ctr
+            yield
+            if sum((v >> (8 * f)) & 0xff for f in range(8)) >= arrivals:
+                break
+            polls += 1
+            if polls > 20_000:
+                timeout = True
+                sync.err = 1
+                break
+        ok = not timeout and ((v >> 0) & 0xff) == arrivals and sync.err == 0
+        passed = sync.done                 # atomic fetch-add with return
+        sync.done += 1
+        yield
+        seen.append((sum((v >> (8 * f)) & 0xff for f in range(8)), ok))
+        yield                              # the items
+        if passed == per_head - 1:         # the last to count clears
+            sync.ctr = 0
+            sync.done = 0
+        yield
+
+    actors = [arriver(o) for o in offsets] + [reducer() for _ in range(per_head)]
+    # dispatch order: signalling blocks first, reduce blocks after (a reduce
+    # block only starts once started; everything runs to completion)
+    started = []
+    pending = list(actors)
+    while pending or started:   # every actor ends: arrivals at once, reducers within their bound
+        if pending and (not started or rng.random() < 0.5):
+            started.append(pending.pop(0))
+        a = started[rng.integers(len(started))]
+        try:
+            next(a)
+        except StopIteration:
+            started.remove(a)
+    return seen
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_reduce_sync_protocol_under_random_interleavings(seed):
+    rng = np.random.default_rng(seed)
+    sync = SyncModel()
+    for launch in range(4):
+        arrivals = int(rng.integers(1, 65))
+        per_head = int(rng.integers(1, 25))
+        seen = run_launch(sync, arrivals, per_head, rng)
+        # every reduce block passed only after all arrivals, and trusted them
+        assert len(seen) == per_head
+        assert all(n == arrivals and ok for n, ok in seen)
+        # the launch leaves the words zero for the next one
+        assert sync.ctr == 0 and sync.done == 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_reduce_sync_protocol_flags_a_block_off_the_xcd_and_the_error_word(seed):
+    rng = np.random.default_rng(100 + seed)
+    sync = SyncModel()
+    offsets = [0] * 20
+    offsets[int(rng.integers(20))] = int(rng.integers(1, 8))   # one block elsewhere
+    seen = run_launch(sync, 20, 6, rng, offsets=offsets)
+    assert seen and not any(ok for _, ok in seen)
+    assert sync.ctr == 0 and sync.done == 0
+    seen = run_launch(sync, 20, 6, rng, err_from_host=True)
+    assert not any(ok for _, ok in seen)
